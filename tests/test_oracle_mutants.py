@@ -1,0 +1,77 @@
+"""Plant plausible mistakes in a copy of the oracle; the pins must catch each.
+
+Each mutant is a textual edit of the oracle's source (a dropped term, a wrong
+sign or index, a transposed operand, an off-by-one in a key set or a cache
+slot).  The edited source is executed as a separate module, on the CPU; the
+real oracle is untouched.
+"""
+import inspect
+import types
+
+import pytest
+
+import oracle.rat_oracle as real
+from tests import oracle_pins
+
+MUTANTS = {
+    "grid aligned at j mod D == 0": (
+        "np.arange(D - 1, t + 1, D", "np.arange(0, t + 1, D"),
+    "window starts one early": (
+        "window = np.arange(max(0, t - W + 1), t + 1",
+        "window = np.arange(max(0, t - W), t + 1"),
+    "window drops the query's own state": (
+        "window = np.arange(max(0, t - W + 1), t + 1,",
+        "window = np.arange(max(0, t - W + 1), t,"),
+    "empty key set falls back to own state": (
+        "return np.union1d(grid, window)",
+        "return np.union1d(np.union1d(grid, window), [t])"),
+    "gate roles swapped": (
+        "h = g * h + c * x[:, t]", "h = c * h + g * x[:, t]"),
+    "initial state dropped": (
+        "h = np.zeros((B, H, Dh)) if h0 is None else np.array(h0, dtype=np.float64)",
+        "h = np.zeros((B, H, Dh))"),
+    "sigmoid sign flipped": (
+        "g = 1.0 / (1.0 + np.exp(-z))", "g = 1.0 / (1.0 + np.exp(z))"),
+    "state emitted before the update": (
+        "h = g * h + c * x[:, t]\n        out[:, t] = h",
+        "out[:, t] = h\n        h = g * h + c * x[:, t]"),
+    "softmax scale dropped": (
+        "s = scale * (K @ q)", "s = (K @ q)"),
+    "softmax not normalised": (
+        "p /= p.sum()\n", "\n"),
+    "keys used as values": (
+        "return p @ V", "return p @ K"),
+    "value states gated by key logits": (
+        "Vt = scan(v, zv, h0v)\n    else", "Vt = scan(v, zk, h0v)\n    else"),
+    "decode grid overlaps the window": (
+        "sel = np.nonzero(gpos <= t - W)[0]", "sel = np.nonzero(gpos <= t - W + 1)[0]"),
+    "decode grid stops one short": (
+        "sel = np.nonzero(gpos <= t - W)[0]", "sel = np.nonzero(gpos < t - W)[0]"),
+    "decode ring slot off by one": (
+        "self.ring_k[b, h, t % W] = self.state_k[b, h]",
+        "self.ring_k[b, h, (t + 1) % W] = self.state_k[b, h]"),
+    "decode grid append index off by one": (
+        "i = (t + 1) // D - 1\n", "i = min((t + 1) // D, self.grid_k[h].shape[1] - 1)\n"),
+    "decode value state gated by key logits": (
+        "gv, cv = gates(zv)", "gv, cv = gates(zk)"),
+}
+
+
+def _mutant(old, new):
+    src = inspect.getsource(real)
+    assert src.count(old) >= 1, f"mutation site not found: {old!r}"
+    src = src.replace(old, new)
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src, "oracle_mutant", "exec"), mod.__dict__)  # noqa: S102
+    return mod
+
+
+def test_real_oracle_passes_every_pin():
+    assert oracle_pins.run_all(real) == []
+
+
+@pytest.mark.parametrize("name", list(MUTANTS))
+def test_mutant_is_caught(name):
+    old, new = MUTANTS[name]
+    failed = oracle_pins.run_all(_mutant(old, new))
+    assert failed, f"no pin catches the mutant: {name}"

@@ -1,0 +1,10 @@
+"""The fp64 oracle against facts other than itself (CPU only)."""
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_pin(pin):
+    pin(oracle.rat_oracle)
