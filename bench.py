@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Benchmark of the RAT+ dilated operator on one MI355X.
+
+Default run: the prefill workload B=1, 16 heads x 128, T=16384, D=16, W=128,
+bf16 (one step = one rat_dilated_prefill call: recurrence over keys and
+values plus dilated attention) gives `value` in tokens/s; the batched decode
+workload (batch 256, 16 x 128, context 32768, D=16, W=64, 1024 steps) is
+measured in the same run and reported under "decode".  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps N]
+                    [--no-decode] [--no-cpu-baseline] [--config N]
+
+--config N (1..5) measures one workload alone (auxiliary).  Inputs are
+seeded synthetic data generated on the GPU and resident in HBM before timing.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
+PEAK_BF16 = 2.5e15         # flop/s, dense bf16 MFMA
+PEAK_F32_VALU = 157.3e12   # flop/s, fp32 vector
+
+CONFIGS = {
+    1: dict(kind="prefill", B=1, H=2, Dh=64, T=1024, D=4, W=0, dtype="f32", mu=2.0),
+    2: dict(kind="prefill", B=1, H=16, Dh=128, T=16384, D=16, W=128, dtype="bf16", mu=2.0),
+    3: dict(kind="prefill", B=1, H=16, Dh=128, T=262144, D=64, W=0, dtype="bf16", mu=3.0),
+    4: dict(kind="decode", B=256, H=16, Dh=128, ctx=32768, D=[16] * 16, W=64, steps=1024, mu=2.0,
+            dtype="bf16"),
+    5: dict(kind="decode", B=128, H=32, Dh=128, ctx=131072, D=[1] * 8 + [16] * 12 + [64] * 12, W=64,
+            steps=1024, mu=2.0, dtype="bf16"),
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# work model (algorithmic bytes and flops; counts from the key-set ranges)
+# ---------------------------------------------------------------------------
+
+def prefill_pairs(T, D, W):
+    import numpy as np
+    t = np.arange(T, dtype=np.int64)
+    grid = np.maximum(0, t - W + 1) // D
+    win = np.minimum(W, t + 1)
+    return int(grid.sum() + win.sum())
+
+
+def prefill_work(c):
+    B, H, Dh, T, D, W = c["B"], c["H"], c["Dh"], c["T"], c["D"], c["W"]
+    e = 2 if c["dtype"] == "bf16" else 4
+    n = B * T * H * Dh
+    scan_read = 2 * n * (e + 4)                    # x and fp32 logits, keys and values
+    scan_write = 2 * n * e if W > 0 else 2 * B * (T // D) * H * Dh * e
+    pairs = prefill_pairs(T, D, W) * B * H
+    flops = 4 * Dh * pairs
+    return dict(scan_bytes=scan_read + scan_write, attn_flops=flops, pairs=pairs)
+
+
+def decode_step_bytes(c, t):
+    """Algorithmic HBM bytes of one decode step with every sequence at position t."""
+    B, H, Dh, W = c["B"], c["H"], c["Dh"], c["W"]
+    e = 2
+    total = 0
+    for D in c["D"]:
+        n_g = max(0, t - W + 1) // D
+        n_w = min(W, t + 1) if W > 0 else 0
+        rows = n_g + max(0, n_w - 1)           # the newest state comes from registers
+        kv = rows * Dh * e * 2
+        state = Dh * 4 * 2 * 2                  # fp32 state read + write, keys and values
+        new = Dh * (3 * e + 2 * 4)              # q, k, v, zk, zv
+        writes = Dh * e * 2 * ((1 if W > 0 else 0) + (1 if (t + 1) % D == 0 else 0))
+        out = Dh * e
+        total += kv + state + new + writes + out
+    return B * total
+
+
+# ---------------------------------------------------------------------------
+# timing helpers
+# ---------------------------------------------------------------------------
+
+def time_loop(fn, steps, torch):
+    """Average ms per call of fn() with HIP events on the current stream."""
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(steps):
+        fn()
+    e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def bench_prefill(c, steps, warmup, torch, R, inputs):
+    dev = "cuda:0"
+    dt = torch.bfloat16 if c["dtype"] == "bf16" else torch.float32
+    log(f"[bench] prefill inputs B={c['B']} T={c['T']} H={c['H']} Dh={c['Dh']} D={c['D']} W={c['W']}")
+    x = inputs.prefill_inputs(c["B"], c["T"], c["H"], c["Dh"], dtype=dt, mu=c["mu"], seed=2, device=dev)
+    out = torch.empty_like(x["q"])
+    ws_bytes = R.rat_dilated_prefill_workspace_size(c["B"], c["T"], c["H"], c["Dh"], c["D"], c["W"], dt)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+    args = (x["q"], x["k"], x["v"], x["zk"], x["zv"], c["D"], c["W"])
+
+    def step():
+        R.rat_dilated_prefill(*args, out=out, ws=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = time_loop(step, steps, torch)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps * 1e3
+    log(f"[bench] prefill {ms:.3f} ms/step (wall {wall:.3f})")
+
+    # per-stage timing (same kernels, launched stage by stage)
+    def scan_only():
+        R.rat_dilated_prefill_stage(1, *args, out=out, ws=ws)
+
+    def attn_only():
+        R.rat_dilated_prefill_stage(2, *args, out=out, ws=ws)
+
+    scan_only()
+    ms_scan = time_loop(scan_only, steps, torch)
+    ms_attn = time_loop(attn_only, steps, torch)
+    err = R.workspace_error(ws)
+    log(f"[bench] stages: scan {ms_scan:.3f} ms, attention {ms_attn:.3f} ms, ws error {err}")
+    return dict(ms=ms, wall_ms=wall, ms_scan=ms_scan, ms_attn=ms_attn, x=x, out=out, ws_error=err)
+
+
+def bench_decode(c, steps, warmup, torch, R, inputs):
+    dev = "cuda:0"
+    B, H, Dh, W = c["B"], c["H"], c["Dh"], c["W"]
+    dil = c["D"]
+    max_pos = c["ctx"] + max(steps, warmup)
+    off, cap, rows = R.rat_grid_layout(H, dil, max_pos)
+    log(f"[bench] decode cache B={B} H={H} ctx={c['ctx']} rows/seq={rows} "
+        f"({2 * B * rows * Dh * 2 / 1e9:.1f} GB)")
+    cache = inputs.decode_cache(B, H, Dh, dil, W, c["ctx"], max(steps, warmup), seed=4, device=dev)
+    assert cache["layout"].cap == cap and cache["layout"].off == off
+    n_in = max(steps, warmup)
+    st = inputs.decode_step_inputs(B, H, Dh, n_in, mu=c["mu"], seed=5, device=dev)
+    pos = torch.full((B,), c["ctx"], dtype=torch.int32, device=dev)
+    out = torch.empty((B, H, Dh), dtype=torch.bfloat16, device=dev)
+    ws = torch.zeros(R.rat_decode_workspace_size(B, H, Dh, dil, W, max_pos), dtype=torch.uint8, device=dev)
+
+    def run(n):
+        for i in range(n):
+            R.rat_decode_step(st["q"][i], st["k"][i], st["v"][i], st["zk"][i], st["zv"][i],
+                              cache["state_k"], cache["state_v"], cache["grid_k"], cache["grid_v"],
+                              off, cap, cache["ring_k"], cache["ring_v"], pos, max_pos, dil, W,
+                              out=out, ws=ws)
+            pos.add_(1)
+
+    run(warmup)
+    torch.cuda.synchronize()
+    pos.fill_(c["ctx"])
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(s)
+    run(steps)
+    e1.record(s)
+    e1.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    err = R.workspace_error(ws)
+    bytes_avg = sum(decode_step_bytes(c, c["ctx"] + i) for i in range(steps)) / steps
+    log(f"[bench] decode {ms:.3f} ms/step, {bytes_avg / (ms * 1e-3) / 1e9:.0f} GB/s, ws error {err}")
+    return dict(ms=ms, wall_s=wall, bytes_per_step=bytes_avg, ws_error=err, steps=steps)
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle as it stands, one thread
+# ---------------------------------------------------------------------------
+
+def cpu_baseline_prefill(c, x, torch):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    f = lambda t: t.float().cpu().double().numpy()  # noqa: E731
+    hs = [0, 1]   # sample: two heads, every query row, full-length recurrence
+    xs = {k: f(v[:, :, hs]) for k, v in x.items()}
+    import contextlib
+    lim = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
+    with lim:
+        t0 = time.perf_counter()
+        oracle.prefill(xs["q"], xs["k"], xs["v"], xs["zk"], xs["zv"], c["D"], c["W"])
+        sec = time.perf_counter() - t0
+    full = sec * c["H"] / len(hs)
+    tok_s = c["B"] * c["T"] / full
+    return dict(value=tok_s, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"oracle prefill of heads {hs} of {c['H']} (all {c['T']} rows, full recurrence) "
+                       f"in {sec:.1f} s on 1 thread; scaled by H/2 to the whole workload")
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--config", type=int, default=0)
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the operator would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import recurrence_augmented_dilated_amd as R
+    from recurrence_augmented_dilated_amd import inputs
+    R.lib()
+
+    cfg_id = a.config or 2
+    c = CONFIGS[cfg_id]
+    result = {"metric": "prefill & decode tokens/s of RAT+ dilated op; % HBM/MFMA roofline",
+              "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True, "scaling": "weak",
+              "vs_baseline": None, "data": "synthetic"}
+
+    if c["kind"] == "prefill":
+        p = bench_prefill(c, a.steps, a.warmup, torch, R, inputs)
+        w = prefill_work(c)
+        tok_s = c["B"] * c["T"] / (p["ms"] * 1e-3)
+        scan_gbs = w["scan_bytes"] / (p["ms_scan"] * 1e-3)
+        attn_tfs = w["attn_flops"] / (p["ms_attn"] * 1e-3)
+        bf16 = c["dtype"] == "bf16"
+        attn_peak = PEAK_BF16 if bf16 else PEAK_F32_VALU
+        kernels = {
+            "scan": {"bound": "hbm", "ms": p["ms_scan"], "achieved": scan_gbs / 1e9, "peak": PEAK_HBM / 1e9,
+                     "unit": "GB/s", "frac": scan_gbs / PEAK_HBM, "algorithmic_bytes": w["scan_bytes"]},
+            "attention": {"bound": "mfma" if bf16 else "alu", "ms": p["ms_attn"], "achieved": attn_tfs / 1e12,
+                          "peak": attn_peak / 1e12, "unit": "TFLOP/s", "frac": attn_tfs / attn_peak,
+                          "algorithmic_flops": w["attn_flops"]},
+        }
+        dom = "scan" if p["ms_scan"] >= p["ms_attn"] else "attention"
+        k = kernels[dom]
+        result.update({
+            "value": tok_s, "steps": a.steps, "warmup": a.warmup, "ms_per_step": p["ms"],
+            "dtype": c["dtype"],
+            "config": {"workload": f"prefill B={c['B']} H={c['H']} Dh={c['Dh']} T={c['T']} D={c['D']} "
+                                   f"W={c['W']} {c['dtype']}", "config_id": cfg_id, "B": c["B"], "T": c["T"],
+                       "heads": c["H"], "head_dim": c["Dh"], "dilation": c["D"], "window": c["W"]},
+            "roofline": {"kernel": dom, "bound": k["bound"], "achieved": k["achieved"], "peak": k["peak"],
+                         "unit": k["unit"], "frac": k["frac"], "traffic": None},
+            "kernels": kernels,
+            "ws_error": p["ws_error"],
+        })
+        if not a.no_decode and a.config == 0:
+            cd = CONFIGS[4]
+            d = bench_decode(cd, a.decode_steps, 8, torch, R, inputs)
+            gbs = d["bytes_per_step"] / (d["ms"] * 1e-3)
+            result["decode"] = {
+                "workload": "decode B=256 H=16 Dh=128 ctx=32768 D=16 W=64 bf16", "steps": d["steps"],
+                "tokens_per_s": cd["B"] / (d["ms"] * 1e-3), "ms_per_step": d["ms"],
+                "roofline": {"bound": "hbm", "achieved": gbs / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                             "frac": gbs / PEAK_HBM}, "ws_error": d["ws_error"]}
+        if not a.no_cpu_baseline:
+            log("[bench] cpu baseline (oracle) ...")
+            result["cpu_baseline"] = cpu_baseline_prefill(c, p["x"], torch)
+    else:
+        d = bench_decode(c, a.decode_steps, 8, torch, R, inputs)
+        gbs = d["bytes_per_step"] / (d["ms"] * 1e-3)
+        result.update({
+            "value": c["B"] / (d["ms"] * 1e-3), "steps": d["steps"], "warmup": 8, "ms_per_step": d["ms"],
+            "dtype": "bf16",
+            "config": {"workload": f"decode B={c['B']} H={c['H']} Dh={c['Dh']} ctx={c['ctx']} "
+                                   f"W={c['W']} dilation={sorted(set(c['D']))}", "config_id": cfg_id},
+            "roofline": {"kernel": "decode", "bound": "hbm", "achieved": gbs / 1e9, "peak": PEAK_HBM / 1e9,
+                         "unit": "GB/s", "frac": gbs / PEAK_HBM, "traffic": None},
+            "ws_error": d["ws_error"],
+        })
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,197 @@
+/*
+ * librat -- the RAT+ temporal-mixing operator on AMD MI355X (gfx950).
+ *
+ * The operator ("RAT+: Train Dense, Infer Sparse -- Recurrence Augmented
+ * Attention for Dilated Inference", abstract and Figs. 1-2; "Augmenting
+ * Attention with Exponentially Decaying Memory Improves Query-Aware KV
+ * Sparsity", sections 2.1-2.2) has two parts:
+ *
+ *   1. a full-sequence, per-channel gated linear recurrence over keys and
+ *      values (an exponentially decaying memory with an input-dependent gate):
+ *          g_t = sigmoid(z_t),   h_t = g_t * h_{t-1} + (1 - g_t) * x_t;
+ *   2. softmax attention of each query t over the recurrent states on the
+ *      dilated grid { j <= t : (j + 1) mod D == 0 } plus, optionally, the
+ *      local window { max(0, t - W + 1) .. t } (a set: counted once), in a
+ *      prefill form and a one-token decode form.  A query with no key yields
+ *      a zero output.  The dilation D may differ per head.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense, row-major, 0-based.  Token tensors are
+ *     [B][T][H][Dh] with Dh innermost; Dh must be 64 or 128; H <= 128.
+ *   - Every buffer argument is DEVICE memory owned by the caller, 16-byte
+ *     aligned.  Array arguments documented as "host" are host memory and are
+ *     read before the call returns.  The library never allocates, frees or
+ *     synchronizes; scratch comes from the caller's workspace.
+ *   - A workspace must be zero-filled once before its first use (e.g. with
+ *     hipMemset) and may then be reused by any number of calls issued in
+ *     stream order.  Two calls that run concurrently need two workspaces.
+ *     Its first 256 bytes are a header; the 32-bit word at byte offset 8 is a
+ *     sticky error word: bit 0 = a scan carry wait exceeded its bound (the
+ *     results of that call are invalid), bit 1 = a decode position was
+ *     outside [0, max_pos) (that sequence's output is zero and its cache is
+ *     untouched).  Zero the word to reset it.
+ *   - All work is asynchronous on `stream`.  The returned status covers
+ *     argument validation (done on the host before any HIP call) and launch
+ *     errors; device faults surface at the caller's next synchronization.
+ *     On an error return nothing was launched unless the status is
+ *     RAT_ERR_HIP.  No exception crosses the ABI.
+ *   - dtype RAT_BF16: q, k, v, states, caches and outputs are bf16
+ *     (round-to-nearest-even), every accumulation is fp32.  RAT_F32: all of
+ *     them are fp32.  Gate logits, recurrent states handed between calls and
+ *     h0 / h_last are always fp32.
+ */
+#ifndef RAT_H_
+#define RAT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RAT_OK = 0,
+  RAT_ERR_INVALID_ARG = -1,  /* null pointer, bad size, misaligned buffer */
+  RAT_ERR_UNSUPPORTED = -2,  /* valid but not implemented (e.g. Dh = 96) */
+  RAT_ERR_WORKSPACE = -3,    /* ws_bytes smaller than the *_workspace_size */
+  RAT_ERR_HIP = -4           /* a HIP launch failed; see rat_last_error() */
+} rat_status_t;
+
+typedef enum { RAT_F32 = 0, RAT_BF16 = 1 } rat_dtype_t;
+
+#define RAT_MAX_HEADS 128
+
+/* Human-readable name of a status code (static string). */
+const char* rat_status_string(rat_status_t status);
+
+/* Detail of the last error on the calling thread (thread-local, static
+ * storage; empty string if none). */
+const char* rat_last_error(void);
+
+/* ------------------------------------------------------------------------ *
+ * rat_scan -- the gated recurrence alone (part 1 above; the recurrence is
+ * full-sequence, L = T: RAT+ Fig. 1a; memory update: follow-up page,
+ * section 2.1).
+ *
+ *   x       [B][T][H][Dh]  dtype         inputs (keys or values)
+ *   z       [B][T][H][Dh]  fp32          gate logits (g = sigmoid(z);
+ *                                        1 - g is evaluated as sigmoid(-z);
+ *                                        +-inf allowed)
+ *   h0      [B][H][Dh]     fp32 or NULL  state before position 0 (NULL: 0)
+ *   states  [B][T/E][H][Dh] dtype or NULL, E = store_every >= 1: entry i
+ *           holds h at position (i + 1) * E - 1, i.e. every state at a
+ *           position j with (j + 1) mod E == 0 (E = 1: all states; E = D:
+ *           the dilated grid)
+ *   h_last  [B][H][Dh]     fp32 or NULL  state at position T - 1
+ *   ws      workspace of at least rat_scan_workspace_size(B, T, H, Dh) bytes
+ * T = 0 is a no-op (buffers may then be NULL).  States and h_last come from
+ * one fp32 carry chain.
+ * ------------------------------------------------------------------------ */
+size_t rat_scan_workspace_size(int32_t B, int32_t T, int32_t H, int32_t Dh);
+rat_status_t rat_scan(const void* x, const float* z, const float* h0, void* states,
+                      int32_t store_every, float* h_last, int32_t B, int32_t T, int32_t H,
+                      int32_t Dh, rat_dtype_t dtype, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * rat_dilated_prefill -- the whole operator over a sequence (RAT+ abstract:
+ * dilated attention over every D-th recurrent state with an optional local
+ * window, per-head dilation allowed; Fig. 1c).
+ *
+ *   q, k, v   [B][T][H][Dh] dtype
+ *   zk, zv    [B][T][H][Dh] fp32   gate logits for keys and for values
+ *   out       [B][T][H][Dh] dtype  o_t = sum_{j in S_t} softmax_j(scale *
+ *                                  <q_t, k~_j>) v~_j  (0 if S_t is empty)
+ *   dilation  host [H]  D per head, D >= 1 (D = 1: causal attention over
+ *                       the recurrent states)
+ *   W         window >= 0 (0: grid only)
+ *   scale     softmax scale; <= 0 selects 1/sqrt(Dh)
+ *   ws        workspace of at least rat_dilated_prefill_workspace_size(...)
+ *             bytes; it receives the recurrent states
+ * The recurrence starts from zero state.  T = 0 is a no-op (buffers may
+ * then be NULL).
+ * ------------------------------------------------------------------------ */
+size_t rat_dilated_prefill_workspace_size(int32_t B, int32_t T, int32_t H, int32_t Dh,
+                                          const int32_t* dilation, int32_t W,
+                                          rat_dtype_t dtype);
+rat_status_t rat_dilated_prefill(const void* q, const void* k, const void* v, const float* zk,
+                                 const float* zv, void* out, int32_t B, int32_t T, int32_t H,
+                                 int32_t Dh, const int32_t* dilation, int32_t W, float scale,
+                                 rat_dtype_t dtype, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
+/* The same operation split into its two stages, for callers that schedule
+ * or time them separately.  RAT_STAGE_RECURRENCE runs the scan of keys and
+ * values into the workspace; RAT_STAGE_ATTENTION runs the attention from a
+ * workspace that a RECURRENCE stage with identical arguments filled earlier
+ * in stream order; RAT_STAGE_ALL equals rat_dilated_prefill. */
+typedef enum {
+  RAT_STAGE_ALL = 0,
+  RAT_STAGE_RECURRENCE = 1,
+  RAT_STAGE_ATTENTION = 2
+} rat_prefill_stage_t;
+rat_status_t rat_dilated_prefill_stage(rat_prefill_stage_t stage, const void* q, const void* k,
+                                       const void* v, const float* zk, const float* zv, void* out,
+                                       int32_t B, int32_t T, int32_t H, int32_t Dh,
+                                       const int32_t* dilation, int32_t W, float scale,
+                                       rat_dtype_t dtype, void* ws, size_t ws_bytes,
+                                       hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Decode cache layout helper.  The grid cache of head h holds grid_cap[h]
+ * entries per sequence, entry i = the state at position (i + 1) * D_h - 1;
+ * all heads share one buffer: head h occupies elements
+ * [B * grid_off[h] * Dh, B * (grid_off[h] + grid_cap[h]) * Dh), laid out
+ * [B][grid_cap[h]][Dh].  This fills grid_off / grid_cap (host [H]) with the
+ * packed layout of capacity max_pos / D_h per head and returns the total
+ * rows per sequence in *rows (so the buffer holds B * rows * Dh elements).
+ * ------------------------------------------------------------------------ */
+rat_status_t rat_grid_layout(int32_t H, const int32_t* dilation, int64_t max_pos,
+                             int64_t* grid_off, int32_t* grid_cap, int64_t* rows);
+
+/* ------------------------------------------------------------------------ *
+ * rat_decode_step -- one new token per sequence (RAT+ Fig. 2: step update of
+ * the recurrence, attention over the cached states; abstract: the grid
+ * cache is D times smaller than a dense cache).
+ *
+ * For every sequence b at position t = pos[b] and head h (dilation D):
+ *   1. state <- g * state + (1 - g) * x for keys and values (fp32);
+ *   2. if W > 0: ring slot t mod W <- the new state (in dtype);
+ *   3. if (t + 1) mod D == 0: grid entry (t + 1) / D - 1 <- the new state;
+ *   4. out = softmax attention of q over grid entries i < max(0,t-W+1)/D
+ *      (strictly older than the window when W > 0) and the ring slots of
+ *      positions max(0, t - W + 1) .. t.
+ * A cache filled by prefilling positions 0 .. t-1 makes this equal to row t
+ * of a prefill over t + 1 tokens.
+ *
+ *   q, k, v      [B][H][Dh] dtype   the new token
+ *   zk, zv       [B][H][Dh] fp32    its gate logits
+ *   state_k/_v   [B][H][Dh] fp32    in/out recurrent states
+ *   grid_k/_v    ragged grid caches (layout above), dtype, in/out
+ *   grid_off     host [H], grid_cap host [H]: the layout; grid_cap[h] must
+ *                be >= max_pos / D_h
+ *   ring_k/_v    [B][H][W][Dh] dtype, in/out (NULL allowed when W = 0)
+ *   pos          device int32 [B], read-only; every pos[b] must lie in
+ *                [0, max_pos) (others: error bit 1, zero output)
+ *   out          [B][H][Dh] dtype
+ *   dilation     host [H]
+ *   ws           workspace of at least rat_decode_workspace_size(...) bytes
+ * The caller advances pos between steps.
+ * ------------------------------------------------------------------------ */
+size_t rat_decode_workspace_size(int32_t B, int32_t H, int32_t Dh, const int32_t* dilation,
+                                 int32_t W, int64_t max_pos);
+rat_status_t rat_decode_step(const void* q, const void* k, const void* v, const float* zk,
+                             const float* zv, float* state_k, float* state_v, void* grid_k,
+                             void* grid_v, const int64_t* grid_off, const int32_t* grid_cap,
+                             void* ring_k, void* ring_v, const int32_t* pos, int64_t max_pos,
+                             void* out, int32_t B, int32_t H, int32_t Dh,
+                             const int32_t* dilation, int32_t W, float scale, rat_dtype_t dtype,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RAT_H_ */

@@ -1,0 +1,258 @@
+"""Python binding of librat, the RAT+ temporal-mixing operator on MI355X.
+
+A thin ctypes layer over the C ABI in include/rat.h: it checks tensor
+devices, dtypes and contiguity, allocates outputs and zero-initialised
+workspaces with torch, and passes raw pointers and torch's current HIP
+stream.  Every step of the operator runs in librat's HIP kernels; there is no
+CPU or PyTorch fallback.  If librat.so is missing the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "RatError", "lib", "rat_scan", "rat_scan_workspace_size", "rat_dilated_prefill",
+    "rat_dilated_prefill_stage",
+    "rat_dilated_prefill_workspace_size", "rat_grid_layout", "rat_decode_step",
+    "rat_decode_workspace_size", "workspace", "workspace_error", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librat.so")
+
+RAT_F32, RAT_BF16 = 0, 1
+_STATUS = {0: "RAT_OK", -1: "RAT_ERR_INVALID_ARG", -2: "RAT_ERR_UNSUPPORTED",
+           -3: "RAT_ERR_WORKSPACE", -4: "RAT_ERR_HIP"}
+
+_lib = None
+_lock = threading.Lock()
+
+
+class RatError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+def lib():
+    """The loaded librat (ctypes.CDLL).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"librat.so not found at {LIB_PATH}: build it with "
+                    "`python -m recurrence_augmented_dilated_amd.build_lib`")
+            L = ctypes.CDLL(LIB_PATH)
+            c_int, c_i64, c_sz, vp, c_f = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                                          ctypes.c_void_p, ctypes.c_float)
+            L.rat_status_string.restype = ctypes.c_char_p
+            L.rat_status_string.argtypes = [c_int]
+            L.rat_last_error.restype = ctypes.c_char_p
+            L.rat_last_error.argtypes = []
+            L.rat_scan_workspace_size.restype = c_sz
+            L.rat_scan_workspace_size.argtypes = [c_int, c_int, c_int, c_int]
+            L.rat_scan.restype = c_int
+            L.rat_scan.argtypes = [vp, vp, vp, vp, c_int, vp, c_int, c_int, c_int, c_int, c_int,
+                                   vp, c_sz, vp]
+            L.rat_dilated_prefill_workspace_size.restype = c_sz
+            L.rat_dilated_prefill_workspace_size.argtypes = [c_int, c_int, c_int, c_int, vp, c_int, c_int]
+            L.rat_dilated_prefill.restype = c_int
+            L.rat_dilated_prefill.argtypes = [vp, vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, vp,
+                                              c_int, c_f, c_int, vp, c_sz, vp]
+            L.rat_dilated_prefill_stage.restype = c_int
+            L.rat_dilated_prefill_stage.argtypes = [c_int, vp, vp, vp, vp, vp, vp, c_int, c_int, c_int,
+                                                    c_int, vp, c_int, c_f, c_int, vp, c_sz, vp]
+            L.rat_grid_layout.restype = c_int
+            L.rat_grid_layout.argtypes = [c_int, vp, c_i64, vp, vp, vp]
+            L.rat_decode_workspace_size.restype = c_sz
+            L.rat_decode_workspace_size.argtypes = [c_int, c_int, c_int, vp, c_int, c_i64]
+            L.rat_decode_step.restype = c_int
+            L.rat_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                          c_i64, vp, c_int, c_int, c_int, vp, c_int, c_f, c_int,
+                                          vp, c_sz, vp]
+            _lib = L
+    return _lib
+
+
+# ---------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------
+
+def _check(status: int):
+    if status != 0:
+        raise RatError(status, lib().rat_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return RAT_BF16
+    if t.dtype == torch.float32:
+        return RAT_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _i32_array(vals):
+    arr = (ctypes.c_int32 * len(vals))(*[int(v) for v in vals])
+    return arr
+
+
+_ws_cache: dict = {}
+
+
+def workspace(nbytes: int, device, key="default") -> torch.Tensor:
+    """A zero-initialised workspace of at least nbytes, cached per (device, key).
+
+    Workspaces are reused by calls in stream order; they are zero-filled once
+    when allocated.
+    """
+    dev = torch.device(device)
+    k = (dev, key)
+    ws = _ws_cache.get(k)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
+        _ws_cache[k] = ws
+    return ws
+
+
+def workspace_error(ws: torch.Tensor) -> int:
+    """The sticky device error word of a workspace (synchronises)."""
+    return int(ws[8:12].view(torch.int32).item())
+
+
+def _per_head(dilation, H):
+    if isinstance(dilation, int):
+        return [dilation] * H
+    d = [int(x) for x in dilation]
+    if len(d) != H:
+        raise ValueError("dilation must be an int or one value per head")
+    return d
+
+
+# ---------------------------------------------------------------------------
+# rat_scan
+# ---------------------------------------------------------------------------
+
+def rat_scan_workspace_size(B, T, H, Dh) -> int:
+    return int(lib().rat_scan_workspace_size(B, T, H, Dh))
+
+
+def rat_scan(x, z, h0=None, store_every=1, states=None, h_last=None, ws=None, want_h_last=False):
+    """Gated recurrence h_t = g_t h_{t-1} + (1 - g_t) x_t over [B, T, H, Dh].
+
+    Returns (states [B, T // store_every, H, Dh] in x's dtype, h_last or None).
+    """
+    B, T, H, Dh = x.shape
+    if states is None:
+        states = torch.empty((B, T // store_every, H, Dh), dtype=x.dtype, device=x.device)
+    if want_h_last and h_last is None:
+        h_last = torch.empty((B, H, Dh), dtype=torch.float32, device=x.device)
+    if z.dtype != torch.float32:
+        raise TypeError("gate logits must be fp32")
+    if ws is None:
+        ws = workspace(rat_scan_workspace_size(B, T, H, Dh), x.device, "scan")
+    _check(lib().rat_scan(_ptr(x), _ptr(z), _ptr(h0), _ptr(states), int(store_every), _ptr(h_last),
+                          B, T, H, Dh, _dtype_code(x), _ptr(ws), ws.numel(), _stream(x.device)))
+    return states, h_last
+
+
+# ---------------------------------------------------------------------------
+# rat_dilated_prefill
+# ---------------------------------------------------------------------------
+
+def rat_dilated_prefill_workspace_size(B, T, H, Dh, dilation, W, dtype=torch.bfloat16) -> int:
+    d = _i32_array(_per_head(dilation, H))
+    code = RAT_BF16 if dtype == torch.bfloat16 else RAT_F32
+    return int(lib().rat_dilated_prefill_workspace_size(B, T, H, Dh, d, W, code))
+
+
+STAGE_ALL, STAGE_RECURRENCE, STAGE_ATTENTION = 0, 1, 2
+
+
+def rat_dilated_prefill(q, k, v, zk, zv, dilation, W=0, scale=None, out=None, ws=None):
+    """Dilated attention over recurrent states; returns out [B, T, H, Dh]."""
+    return rat_dilated_prefill_stage(STAGE_ALL, q, k, v, zk, zv, dilation, W, scale, out, ws)
+
+
+def rat_dilated_prefill_stage(stage, q, k, v, zk, zv, dilation, W=0, scale=None, out=None, ws=None):
+    """One stage (0 all, 1 recurrence, 2 attention) of rat_dilated_prefill."""
+    B, T, H, Dh = q.shape
+    for t in (k, v):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v must share shape and dtype")
+    for t in (zk, zv):
+        if t.shape != q.shape or t.dtype != torch.float32:
+            raise ValueError("zk, zv must be fp32 with q's shape")
+    dil = _per_head(dilation, H)
+    if out is None:
+        out = torch.empty_like(q)
+    if ws is None:
+        ws = workspace(rat_dilated_prefill_workspace_size(B, T, H, Dh, dil, W, q.dtype), q.device, "prefill")
+    s = -1.0 if scale is None else float(scale)
+    _check(lib().rat_dilated_prefill_stage(int(stage), _ptr(q), _ptr(k), _ptr(v), _ptr(zk), _ptr(zv),
+                                           _ptr(out), B, T, H, Dh, _i32_array(dil), int(W), s,
+                                           _dtype_code(q), _ptr(ws), ws.numel(), _stream(q.device)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+
+def rat_grid_layout(H, dilation, max_pos):
+    """(grid_off list, grid_cap list, rows per sequence) of the ragged grid cache."""
+    dil = _per_head(dilation, H)
+    off = (ctypes.c_int64 * H)()
+    cap = (ctypes.c_int32 * H)()
+    rows = ctypes.c_int64()
+    _check(lib().rat_grid_layout(H, _i32_array(dil), int(max_pos), off, cap, ctypes.byref(rows)))
+    return list(off), list(cap), int(rows.value)
+
+
+def rat_decode_workspace_size(B, H, Dh, dilation, W, max_pos) -> int:
+    return int(lib().rat_decode_workspace_size(B, H, Dh, _i32_array(_per_head(dilation, H)), W, int(max_pos)))
+
+
+def rat_decode_step(q, k, v, zk, zv, state_k, state_v, grid_k, grid_v, grid_off, grid_cap,
+                    ring_k, ring_v, pos, max_pos, dilation, W, scale=None, out=None, ws=None):
+    """One decode step (mutates state, ring and grid caches); returns out [B, H, Dh]."""
+    B, H, Dh = q.shape
+    dil = _per_head(dilation, H)
+    if pos.dtype != torch.int32:
+        raise TypeError("pos must be int32")
+    if out is None:
+        out = torch.empty_like(q)
+    if ws is None:
+        ws = workspace(rat_decode_workspace_size(B, H, Dh, dil, W, max_pos), q.device, "decode")
+    off = (ctypes.c_int64 * H)(*[int(x) for x in grid_off])
+    cap = _i32_array(grid_cap)
+    s = -1.0 if scale is None else float(scale)
+    _check(lib().rat_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(zk), _ptr(zv), _ptr(state_k), _ptr(state_v), _ptr(grid_k),
+        _ptr(grid_v), off, cap, _ptr(ring_k), _ptr(ring_v), _ptr(pos), int(max_pos), _ptr(out), B, H,
+        Dh, _i32_array(dil), int(W), s, _dtype_code(q), _ptr(ws), ws.numel(), _stream(q.device)))
+    return out
+
+
+def default_scale(Dh: int) -> float:
+    return 1.0 / math.sqrt(Dh)

@@ -1,0 +1,146 @@
+// Internal declarations shared by the HIP kernels and the C-ABI host layer of
+// librat.  gfx950 (CDNA4) only: wave64, bf16 MFMA, hardware bf16 conversion.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rat {
+
+constexpr int kMaxHeads = 128;
+
+// ---------------------------------------------------------------------------
+// bf16 helpers (storage is raw uint16_t; arithmetic is fp32)
+// ---------------------------------------------------------------------------
+typedef uint16_t bf16_t;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 (one v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float round_bf16(float x) {
+  return bf16_lo(pack_bf16x2(x, 0.f) & 0xffffu);
+}
+
+// ---------------------------------------------------------------------------
+// gate: (g, 1-g) = (sigmoid(z), sigmoid(-z)) without cancellation.
+// With e = exp(-|z|) in (0, 1]: sigmoid(|z|) = 1/(1+e), sigmoid(-|z|) = e/(1+e).
+// z = +inf gives (1, 0), z = -inf gives (0, 1); NaN propagates.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void gate_pair(float z, float& g, float& c) {
+  const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * fabsf(z));
+  const float big = __builtin_amdgcn_rcpf(1.0f + e);
+  const float small = e * big;
+  const bool pos = z >= 0.0f;
+  g = pos ? big : small;
+  c = pos ? small : big;
+}
+
+// ---------------------------------------------------------------------------
+// Per-head tables, passed by value as kernel arguments.
+// grid rows of head h live at element offset B*goff[h]*Dh, laid out
+// [B][gcap[h]][Dh].
+// ---------------------------------------------------------------------------
+struct HeadTable {
+  int32_t dil[kMaxHeads];
+  int32_t gcap[kMaxHeads];
+  int64_t goff[kMaxHeads];
+};
+
+// Element offset of grid row i of (b, h).
+__device__ __forceinline__ int64_t grid_row_offset(const HeadTable& ht, int B, int b, int h,
+                                                   int64_t i, int Dh) {
+  return ((int64_t)B * ht.goff[h] + (int64_t)b * ht.gcap[h] + i) * Dh;
+}
+
+// Workspace header (first 256 bytes of every workspace).
+struct WsHeader {
+  uint32_t ticket;   // scan: next chunk ticket (reset each call)
+  uint32_t epoch;    // scan: call counter; tags published carries
+  uint32_t error;    // sticky bit set: a device-side check failed (see rat.h)
+  uint32_t pad[61];
+};
+static_assert(sizeof(WsHeader) == 256, "header size");
+
+constexpr uint32_t kErrScanSpin = 1u;     // look-back wait exceeded its bound
+constexpr uint32_t kErrDecodePos = 2u;    // decode position outside [0, max_pos)
+
+// ---------------------------------------------------------------------------
+// Launchers (host side, defined in the .hip files)
+// ---------------------------------------------------------------------------
+enum GridMode { kGridToken = 0, kGridHead = 1 };
+
+struct ScanTensor {
+  const void* x;       // [B][T][H][Dh] (f32 or bf16)
+  const float* z;      // [B][T][H][Dh]
+  const float* h0;     // [B][H][Dh] or null
+  void* out_all;       // [B][T][H][Dh] (input dtype) or null
+  void* out_grid;      // grid states (input dtype) or null
+  float* h_last;       // [B][H][Dh] or null
+};
+
+struct ScanPlan {
+  ScanTensor ten[2];
+  int ntensors;
+  int B, T, H, Dh;
+  int bf16;            // 1: x and outputs are bf16; 0: fp32
+  int grid_mode;       // kGridToken (uniform D, [B][T/D][H][Dh]) or kGridHead
+  HeadTable heads;
+  void* ws;            // workspace base (header + look-back arrays)
+};
+
+size_t scan_workspace_bytes(int ntensors, int B, int T, int H, int Dh);
+hipError_t launch_scan(const ScanPlan& p, hipStream_t s);
+
+struct AttnPlan {
+  const void* q;       // [B][T][H][Dh]
+  void* out;           // [B][T][H][Dh]
+  const void* grid_k;  // ragged head-major grid states
+  const void* grid_v;
+  const void* all_k;   // [B][T][H][Dh] states (needed when W > 0)
+  const void* all_v;
+  int B, T, H, Dh, W;
+  int bf16;
+  float scale;
+  HeadTable heads;
+};
+hipError_t launch_prefill_attention(const AttnPlan& p, hipStream_t s);
+
+struct DecodeHeads {
+  HeadTable t;                   // dilation, grid capacity and grid offset by head
+  int32_t nsplit[kMaxHeads];     // splits of one (b, h) item, by head
+  int32_t order[kMaxHeads];      // heads in launch order (heaviest first)
+  int32_t item_base[kMaxHeads + 1];  // first item of order[i]
+};
+
+struct DecodePlan {
+  const void* q; const void* k; const void* v;   // [B][H][Dh]
+  const float* zk; const float* zv;              // [B][H][Dh]
+  float* state_k; float* state_v;                // [B][H][Dh]
+  void* grid_k; void* grid_v;                    // ragged head-major
+  void* ring_k; void* ring_v;                    // [B][H][W][Dh]
+  const int32_t* pos;                            // [B]
+  int64_t max_pos;
+  void* out;                                     // [B][H][Dh]
+  int B, H, Dh, W;
+  int bf16;
+  float scale;
+  DecodeHeads heads;
+  int n_items;
+  int any_split;
+  float* partials;                               // [B*H*maxsplit][Dh+2]
+  int max_split;
+  uint32_t* hdr;
+};
+hipError_t launch_decode(const DecodePlan& p, hipStream_t s);
+
+}  // namespace rat

@@ -1,0 +1,111 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import recurrence_augmented_dilated_amd as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "rat.h")).read()
+    return sorted(set(re.findall(r"\b(rat_[a-z_]+)\s*\(", src)))
+
+
+def test_header_symbols_exported():
+    L = R.lib()
+    names = _declared()
+    assert "rat_scan" in names and "rat_dilated_prefill" in names and "rat_decode_step" in names
+    for n in names:
+        assert hasattr(L, n), f"librat.so does not export {n}"
+
+
+def test_status_strings():
+    L = R.lib()
+    assert L.rat_status_string(0) == b"RAT_OK"
+    assert L.rat_status_string(-3) == b"RAT_ERR_WORKSPACE"
+
+
+FAKE = ctypes.c_void_p(0x10000)      # aligned, never dereferenced: validation fails first
+MIS = ctypes.c_void_p(0x10004)       # misaligned
+
+
+def _scan(**kw):
+    a = dict(x=FAKE, z=FAKE, h0=None, states=FAKE, E=1, hl=None, B=1, T=16, H=2, Dh=64, dt=0,
+             ws=FAKE, wsb=0)
+    a.update(kw)
+    return R.lib().rat_scan(a["x"], a["z"], a["h0"], a["states"], a["E"], a["hl"], a["B"], a["T"],
+                            a["H"], a["Dh"], a["dt"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), -1), (dict(z=None), -1), (dict(x=MIS), -1), (dict(Dh=96), -2),
+    (dict(B=0), -1), (dict(T=-1), -1), (dict(H=0), -1), (dict(H=129), -1), (dict(E=0), -1),
+    (dict(dt=7), -1), (dict(ws=None), -1), (dict(wsb=16), -3),
+])
+def test_scan_validation(kw, code):
+    assert _scan(**kw) == code
+    assert R.lib().rat_last_error() != b""
+
+
+def _prefill(dil=(4, 4), W=0, wsb=0, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, zk=FAKE, zv=FAKE, out=FAKE, B=1, T=64, H=2, Dh=128, dt=1,
+             ws=FAKE)
+    a.update(kw)
+    d = (ctypes.c_int32 * len(dil))(*dil) if dil is not None else None
+    return R.lib().rat_dilated_prefill(a["q"], a["k"], a["v"], a["zk"], a["zv"], a["out"], a["B"],
+                                       a["T"], a["H"], a["Dh"], d, W, -1.0, a["dt"], a["ws"], wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dil=(0, 4)), -1), (dict(dil=None), -1), (dict(W=-1), -1), (dict(q=None), -1),
+    (dict(out=MIS), -1), (dict(Dh=32), -2), (dict(wsb=100), -3),
+])
+def test_prefill_validation(kw, code):
+    assert _prefill(**kw) == code
+
+
+def test_stage_validation():
+    d = (ctypes.c_int32 * 2)(4, 4)
+    st = R.lib().rat_dilated_prefill_stage(9, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 2, 128, d, 0,
+                                           -1.0, 1, FAKE, 1 << 30, None)
+    assert st == -1
+
+
+def test_decode_validation():
+    L = R.lib()
+    H = 2
+    d = (ctypes.c_int32 * H)(4, 4)
+    off = (ctypes.c_int64 * H)(0, 25)
+    cap_ok = (ctypes.c_int32 * H)(25, 25)
+    cap_bad = (ctypes.c_int32 * H)(24, 25)
+
+    def call(cap=cap_ok, W=4, ring=FAKE, max_pos=100, wsb=0, pos=FAKE):
+        return L.rat_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, off, cap, ring, ring,
+                                 pos, max_pos, FAKE, 1, H, 128, d, W, -1.0, 1, FAKE, wsb, None)
+
+    assert call(cap=cap_bad) == -1          # grid capacity below max_pos / D
+    assert call(ring=None) == -1            # W > 0 needs ring buffers
+    assert call(max_pos=0) == -1
+    assert call(pos=None) == -1
+    assert call() == -3                     # workspace too small
+    assert call(W=-2) == -1
+
+
+def test_workspace_sizes():
+    assert R.rat_scan_workspace_size(1, 1024, 2, 64) > 256
+    a = R.rat_dilated_prefill_workspace_size(1, 16384, 16, 128, 16, 0)
+    b = R.rat_dilated_prefill_workspace_size(1, 16384, 16, 128, 16, 128)
+    assert b > a > 0
+    assert R.rat_decode_workspace_size(256, 16, 128, 16, 64, 32768 + 1024) > 256
+
+
+def test_grid_layout():
+    off, cap, rows = R.rat_grid_layout(3, [1, 16, 64], 131072 + 1024)
+    assert cap == [132096, 8256, 2064]
+    assert off == [0, 132096, 132096 + 8256]
+    assert rows == sum(cap)
