@@ -26,10 +26,9 @@
  *     hipMemset) and may then be reused by any number of calls issued in
  *     stream order.  Two calls that run concurrently need two workspaces.
  *     Its first 256 bytes are a header; the 32-bit word at byte offset 8 is a
- *     sticky error word: bit 0 = a scan carry wait exceeded its bound (the
- *     results of that call are invalid), bit 1 = a decode position was
- *     outside [0, max_pos) (that sequence's output is zero and its cache is
- *     untouched).  Zero the word to reset it.
+ *     sticky error word: bit 1 = a decode position was outside [0, max_pos)
+ *     (that sequence's output is zero and its cache is untouched).  Zero the
+ *     word to reset it.
  *   - All work is asynchronous on `stream`.  The returned status covers
  *     argument validation (done on the host before any HIP call) and launch
  *     errors; device faults surface at the caller's next synchronization.

@@ -34,9 +34,9 @@
 namespace rat {
 namespace {
 
-constexpr int kBM = 128;      // queries per block (bf16 kernel)
+constexpr int kWaves = 8;     // waves per block (bf16 kernel), 32 queries each
+constexpr int kBM = 32 * kWaves;  // queries per block
 constexpr int kBN = 64;       // keys per tile
-constexpr int kKRow = 136;    // LDS K row: 128 bf16 + 8 pad (272 B)
 
 struct AttnArgs {
   const void* q;
@@ -46,6 +46,7 @@ struct AttnArgs {
   const void* all_k;
   const void* all_v;
   int B, T, H, W;
+  int64_t tpad;               // row length of the transposed all-states V
   int n_qtiles;
   float sl2;                  // softmax scale * log2(e)
   HeadTable heads;
@@ -78,28 +79,68 @@ __device__ __forceinline__ void block_coords(int bid, int B, int H, int n_qtiles
   h = p - b * H;
 }
 
-__device__ __forceinline__ int vt_swz(int d) { return 2 * ((d ^ (d >> 3)) & 15); }
 
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel
 // ---------------------------------------------------------------------------
-template <int DH>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnArgs a) {
-  constexpr int KS = DH / 16;            // MFMA k-steps over the head dim
-  constexpr int DB = DH / 32;            // 32-wide d blocks of O^T
-  constexpr int CH = DH / 8;             // 16-byte chunks per row
-  constexpr int KT = (kBN * CH) / 256;   // K staging tasks per thread
-  constexpr int VT = (kBN / 2 * CH) / 256;  // V staging tasks (key pairs) per thread
-  static_assert(KT >= 1 && VT >= 1, "tile shape");
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(1))) void gbl_void_t;
 
-  __shared__ __attribute__((aligned(16))) bf16_t sK[kBN * kKRow];
-  __shared__ __attribute__((aligned(16))) uint32_t sVt[DH * (kBN / 2)];
+// 16 bytes per lane straight from global memory into LDS: lane l of the wave
+// writes dst + 16 * l (dst must be wave-uniform).  Written as asm so that the
+// compiler does not treat every later LDS read as dependent on it (it cannot
+// prove the ring stages disjoint and would wait for all loads in flight);
+// the instruction has no destination register, and the kernel waits on
+// vmcnt itself before a stage is read.
+__device__ __forceinline__ void load_lds16(const void* src, void* dst) {
+  const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)dst));
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory");
+}
+
+// Wait until at most n of this wave's vector-memory operations are pending.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8));
+}
+
+// Ring barrier: this wave's LDS reads are complete, then all waves meet.  A
+// bare s_barrier (no release fence: that would also drain the prefetches in
+// flight); the empty asm statements keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int DH>
+__global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArgs a) {
+  constexpr int KS = DH / 16;                 // MFMA k-steps over the head dim
+  constexpr int DB = DH / 32;                 // 32-wide d blocks of O^T
+  constexpr int KROW = DH * 2;                // bytes per K row
+  constexpr int LPR = KROW / 16;              // lanes per K row in a direct load
+  constexpr int KBYTES = kBN * KROW;          // K tile
+  constexpr int VBYTES = DH * kBN * 2;        // V^T tile: DH rows of 64 keys
+  constexpr int KL = KBYTES / 1024 / kWaves;  // direct loads per wave per tile
+  constexpr int VL = VBYTES / 1024 / kWaves;
+  static_assert(KL >= 1 && VL >= 1 && KL * kWaves * 1024 == KBYTES && VL * kWaves * 1024 == VBYTES, "tiles");
+
+  // three-stage ring: tile it is read from stage it % 3 while tiles it+1 and
+  // it+2 are in flight into the other two
+  __shared__ __attribute__((aligned(1024))) char sK0[KBYTES];
+  __shared__ __attribute__((aligned(1024))) char sK1[KBYTES];
+  __shared__ __attribute__((aligned(1024))) char sK2[KBYTES];
+  __shared__ __attribute__((aligned(1024))) char sV0[VBYTES];
+  __shared__ __attribute__((aligned(1024))) char sV1[VBYTES];
+  __shared__ __attribute__((aligned(1024))) char sV2[VBYTES];
 
   int b, h, qtile;
   block_coords(blockIdx.x, a.B, a.H, a.n_qtiles, b, h, qtile);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31;
   const int g = lane >> 5;
   const int T = a.T, H = a.H, W = a.W;
@@ -122,78 +163,55 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnArgs a) {
     }
   }
 
-  // key ranges of the block
+  // key ranges of the block (window tiles start on a 64-key boundary)
   const int ng_hi = n_grid(t_last, W, D);
-  const int ng_lo = n_grid(t0, W, D);
   const int ng_me = q_live ? n_grid(tq, W, D) : 0;
   const int ntile_g = (ng_hi + kBN - 1) / kBN;
-  const int j_lo = W > 0 ? max(0, t0 - W + 1) : 0;
-  const int ntile_w = W > 0 ? (t_last - j_lo + kBN) / kBN : 0;
+  const int j_lo = W > 0 ? max(0, t0 - W + 1) / kBN * kBN : 0;
+  const int ntile_w = W > 0 ? (t_last - j_lo) / kBN + 1 : 0;
   const int ntiles = ntile_g + ntile_w;
   const int win_lo_me = max(0, tq - W + 1);
+  // this wave's query range: tiles that are fully masked for it are skipped
+  const int tw0 = t0 + wave * 32;
+  const int tw1 = min(tw0 + 31, T - 1);
+  const bool wave_live = tw0 < T;
+  const int ng_w0 = wave_live ? n_grid(tw0, W, D) : 0;
+  const int ng_w1 = wave_live ? n_grid(tw1, W, D) : 0;
 
+  const int cap = a.heads.gcap[h];
   const bf16_t* gk = static_cast<const bf16_t*>(a.grid_k) + grid_row_offset(a.heads, a.B, b, h, 0, DH);
-  const bf16_t* gv = static_cast<const bf16_t*>(a.grid_v) + grid_row_offset(a.heads, a.B, b, h, 0, DH);
+  const bf16_t* gvt = static_cast<const bf16_t*>(a.grid_v) + grid_row_offset(a.heads, a.B, b, h, 0, DH);
   const bf16_t* ak = W > 0 ? static_cast<const bf16_t*>(a.all_k) + (int64_t)b * T * rowC + h * DH : nullptr;
-  const bf16_t* av = W > 0 ? static_cast<const bf16_t*>(a.all_v) + (int64_t)b * T * rowC + h * DH : nullptr;
+  const bf16_t* avt = W > 0 ? static_cast<const bf16_t*>(a.all_v) + ((int64_t)b * H + h) * DH * a.tpad : nullptr;
 
-  uint4 kreg[KT];
-  uint4 vreg[VT][2];
-
-  auto prefetch = [&](int it) {
+  // issue the direct loads of tile `it` into (dK, dV)
+  auto issue = [&](int it, char* dK, char* dV) {
     const bf16_t* kb;
     const bf16_t* vb;
-    int64_t stride;
+    int64_t kstride, vstride;
     int row0, nvalid;
     if (it < ntile_g) {
-      kb = gk; vb = gv; stride = DH; row0 = it * kBN; nvalid = ng_hi - row0;
+      row0 = it * kBN;
+      kb = gk; kstride = DH; nvalid = ng_hi - row0;
+      vb = gvt; vstride = cap;
     } else {
-      kb = ak; vb = av; stride = rowC; row0 = j_lo + (it - ntile_g) * kBN; nvalid = t_last + 1 - row0;
+      row0 = j_lo + (it - ntile_g) * kBN;
+      kb = ak; kstride = rowC; nvalid = t_last + 1 - row0;
+      vb = avt; vstride = a.tpad;
     }
 #pragma unroll
-    for (int k = 0; k < KT; ++k) {
-      const int task = tid + 256 * k;
-      const int c = task % CH;
-      const int r = task / CH;
-      kreg[k] = r < nvalid ? *reinterpret_cast<const uint4*>(kb + (int64_t)(row0 + r) * stride + 8 * c)
-                           : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < KL; ++u) {
+      const int j = wave * KL + u;                 // 1 KB slice of the tile
+      const int r = j * (64 / LPR) + lane / LPR;   // key row
+      const int p = lane % LPR;                    // physical 16-byte chunk
+      const int c = p ^ (r & 7);                   // logical chunk stored there
+      load_lds16(kb + (int64_t)(row0 + min(r, nvalid - 1)) * kstride + 8 * c, dK + j * 1024);
     }
 #pragma unroll
-    for (int k = 0; k < VT; ++k) {
-      const int task = tid + 256 * k;
-      const int c = task % CH;
-      const int kp = task / CH;
-      const int r = 2 * kp;
-      vreg[k][0] = r < nvalid ? *reinterpret_cast<const uint4*>(vb + (int64_t)(row0 + r) * stride + 8 * c)
-                              : make_uint4(0, 0, 0, 0);
-      vreg[k][1] = r + 1 < nvalid ? *reinterpret_cast<const uint4*>(vb + (int64_t)(row0 + r + 1) * stride + 8 * c)
-                                  : make_uint4(0, 0, 0, 0);
-    }
-  };
-
-  auto commit = [&]() {
-#pragma unroll
-    for (int k = 0; k < KT; ++k) {
-      const int task = tid + 256 * k;
-      const int c = task % CH;
-      const int r = task / CH;
-      *reinterpret_cast<uint4*>(sK + r * kKRow + 8 * c) = kreg[k];
-    }
-#pragma unroll
-    for (int k = 0; k < VT; ++k) {
-      const int task = tid + 256 * k;
-      const int c = task % CH;
-      const int kp = task / CH;
-      const uint32_t w0[4] = {vreg[k][0].x, vreg[k][0].y, vreg[k][0].z, vreg[k][0].w};
-      const uint32_t w1[4] = {vreg[k][1].x, vreg[k][1].y, vreg[k][1].z, vreg[k][1].w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int d = 8 * c + i;
-        // low half: key 2kp, high half: key 2kp+1, head dim d
-        const uint32_t packed = (i & 1) ? __builtin_amdgcn_perm(w1[i >> 1], w0[i >> 1], 0x07060302u)
-                                        : __builtin_amdgcn_perm(w1[i >> 1], w0[i >> 1], 0x05040100u);
-        sVt[d * (kBN / 2) + (kp ^ vt_swz(d))] = packed;
-      }
+    for (int u = 0; u < VL; ++u) {
+      const int j = wave * VL + u;
+      const int d = j * 8 + lane / 8;              // head-dim row of V^T
+      load_lds16(vb + (int64_t)d * vstride + row0 + 8 * (lane % 8), dV + j * 1024);
     }
   };
 
@@ -205,47 +223,45 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnArgs a) {
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  if (ntiles > 0) prefetch(0);
-  for (int it = 0; it < ntiles; ++it) {
-    __syncthreads();
-    commit();
-    __syncthreads();
-    if (it + 1 < ntiles) prefetch(it + 1);
+  auto compute = [&](int it, const char* cK, const char* cV) {
+    const bool is_grid = it < ntile_g;
+    bool needed, masked;
+    int kbase;   // grid index or position of the tile's first key
+    if (is_grid) {
+      kbase = it * kBN;
+      needed = wave_live && kbase < ng_w1;
+      masked = kbase + kBN > ng_w0;
+    } else {
+      kbase = j_lo + (it - ntile_g) * kBN;
+      needed = wave_live && kbase <= tw1 && kbase + kBN - 1 >= max(0, tw0 - W + 1);
+      masked = !(kbase >= tw1 - W + 1 && kbase + kBN - 1 <= tw0);
+    }
+    if (!needed) return;
 
     // ---- S^T = K Q^T for two 32-key blocks
     floatx16_t s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      const int m = 32 * kb + n;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const uint4 w = *reinterpret_cast<const uint4*>(sK + (32 * kb + n) * kKRow + 16 * ks + 8 * g);
+        const int c = (2 * ks + g) ^ (m & 7);
+        const uint4 w = *reinterpret_cast<const uint4*>(cK + m * KROW + 16 * c);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), qf[ks], s[kb], 0, 0, 0);
       }
     }
 
-    // ---- mask (boundary grid tile, every window tile)
-    const bool is_grid = it < ntile_g;
-    if (is_grid) {
-      const int i0 = it * kBN;
-      if (i0 + kBN > ng_lo) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kk = 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (i0 + kk >= ng_me) s[kb][r] = -INFINITY;
-          }
-      }
-    } else {
-      const int j0 = j_lo + (it - ntile_g) * kBN;
+    // ---- mask
+    if (masked) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int j = j0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (j < win_lo_me || j > tq) s[kb][r] = -INFINITY;
+          const int j = kbase + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+          const bool ok = is_grid ? j < ng_me : (j >= win_lo_me && j <= tq);
+          if (!ok) s[kb][r] = -INFINITY;
         }
     }
 
@@ -258,7 +274,15 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnArgs a) {
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx * a.sl2);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    // rescale only when some row of the wave raised its running max
+    if (__ballot(m_new != m_run) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+    }
     m_run = m_new;
     float psum = 0.f;
 #pragma unroll
@@ -269,11 +293,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnArgs a) {
         s[kb][r] = p;
         psum += p;
       }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int i = 0; i < DB; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+    l_run += psum;
 
     // ---- O^T += V^T P^T over four 16-key steps
 #pragma unroll
@@ -286,18 +306,49 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnArgs a) {
       pw.z = pack_bf16x2(s[kb][r0 + 4], s[kb][r0 + 5]);
       pw.w = pack_bf16x2(s[kb][r0 + 6], s[kb][r0 + 7]);
       const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
-      const int kp0 = 8 * st + 2 * g;      // keys 16st + 4g .. +3
-      const int kp1 = kp0 + 4;             // keys 16st + 8 + 4g .. +3
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int d = 32 * db + n;
-        const int sw = vt_swz(d);
-        const uint2 lo = *reinterpret_cast<const uint2*>(sVt + d * (kBN / 2) + (kp0 ^ sw));
-        const uint2 hi = *reinterpret_cast<const uint2*>(sVt + d * (kBN / 2) + (kp1 ^ sw));
+        const char* row = cV + d * (kBN * 2);
+        const uint2 lo = *reinterpret_cast<const uint2*>(row + 2 * col_key_pos(16 * st + 4 * g, d));
+        const uint2 hi = *reinterpret_cast<const uint2*>(row + 2 * col_key_pos(16 * st + 8 + 4 * g, d));
         const uint4 vw = make_uint4(lo.x, lo.y, hi.x, hi.y);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vw), pf, o[db], 0, 0, 0);
       }
     }
+  };
+
+  constexpr int LPW = KL + VL;   // direct loads per wave per tile
+  // one pipeline step: prefetch tile it+2, consume tile it, make tile it+1 visible
+  // The stage pointers are __restrict__ so that, once inlined, the direct
+  // loads into (nK, nV) and the reads of (cK, cV) carry disjoint alias
+  // scopes and the compiler need not wait for the in-flight tile before
+  // reading the current one.
+  auto step = [&](int it, const char* __restrict__ cK, const char* __restrict__ cV, char* __restrict__ nK,
+                  char* __restrict__ nV) {
+    const bool pre = it + 2 < ntiles;
+    if (pre) issue(it + 2, nK, nV);
+    compute(it, cK, cV);
+    if (pre) wait_vmcnt<LPW>();   // tile it+1 has landed; tile it+2 may fly
+    else wait_vmcnt<0>();
+    ring_barrier();
+  };
+
+  wait_vmcnt<0>();   // Q fragments are in registers before the ring starts
+  if (ntiles > 0) {
+    issue(0, sK0, sV0);
+    if (ntiles > 1) {
+      issue(1, sK1, sV1);
+      wait_vmcnt<LPW>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    ring_barrier();
+  }
+  for (int it = 0; it < ntiles; it += 3) {
+    step(it, sK0, sV0, sK2, sV2);
+    if (it + 1 < ntiles) step(it + 1, sK1, sV1, sK0, sV0);
+    if (it + 2 < ntiles) step(it + 2, sK2, sV2, sK1, sV1);
   }
 
   // ---- normalise and store (empty key set -> zeros)
@@ -436,6 +487,7 @@ hipError_t launch_prefill_attention(const AttnPlan& p, hipStream_t s) {
   a.grid_k = p.grid_k; a.grid_v = p.grid_v;
   a.all_k = p.all_k; a.all_v = p.all_v;
   a.B = p.B; a.T = p.T; a.H = p.H; a.W = p.W;
+  a.tpad = p.tpad;
   a.sl2 = p.scale * 1.4426950408889634f;
   a.heads = p.heads;
   const int BH = p.B * p.H;
@@ -443,9 +495,9 @@ hipError_t launch_prefill_attention(const AttnPlan& p, hipStream_t s) {
     a.n_qtiles = (p.T + kBM - 1) / kBM;
     const int blocks = xcd_padded_blocks(BH, a.n_qtiles);
     if (p.Dh == 128)
-      hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(blocks), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(blocks), dim3(kWaves * 64), 0, s, a);
     else
-      hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(blocks), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(blocks), dim3(kWaves * 64), 0, s, a);
   } else {
     a.n_qtiles = (p.T + 63) / 64;
     const int blocks = xcd_padded_blocks(BH, a.n_qtiles);

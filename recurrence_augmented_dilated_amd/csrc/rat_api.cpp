@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "rat_internal.h"
@@ -58,34 +59,50 @@ rat_status_t check_dilation(const int32_t* dilation, int32_t H) {
   return RAT_OK;
 }
 
-// Grid rows per head after T prefill tokens: T / D_h, packed head after head.
-void prefill_grid_layout(int32_t T, int32_t H, const int32_t* dilation, rat::HeadTable& ht,
-                         int64_t& rows) {
+// Prefill workspace layout.  Grid states of head h: T / D_h entries per
+// sequence; the bf16 path pads every head's capacity to a multiple of 64
+// keys (whole attention tiles) and keeps values transposed (kGridHeadCol),
+// keys row-major (kGridHeadRow); the fp32 path keeps both row-major.
+void prefill_grid_layout(int32_t T, int32_t H, const int32_t* dilation, bool bf16,
+                         rat::HeadTable& ht, int64_t& rows) {
   rows = 0;
   std::memset(&ht, 0, sizeof(ht));
   for (int h = 0; h < H; ++h) {
+    const int32_t G = T / dilation[h];
     ht.dil[h] = dilation[h];
-    ht.gcap[h] = T / dilation[h];
+    ht.gcap[h] = bf16 ? (G + 63) / 64 * 64 : G;
     ht.goff[h] = rows;
     rows += ht.gcap[h];
   }
 }
 
+int64_t prefill_tpad(int32_t T) { return ((int64_t)T + 63) / 64 * 64; }
+
 struct PrefillCarve {
-  size_t scan_bytes, grid_bytes, all_bytes, total;
+  size_t scan_bytes, grid_bytes, allk_bytes, allv_bytes, total;
 };
 
 PrefillCarve prefill_carve(int32_t B, int32_t T, int32_t H, int32_t Dh, const int32_t* dilation,
                            int32_t W, rat_dtype_t dt) {
   rat::HeadTable ht;
   int64_t rows;
-  prefill_grid_layout(T, H, dilation, ht, rows);
+  const bool bf16 = dt == RAT_BF16;
+  prefill_grid_layout(T, H, dilation, bf16, ht, rows);
   PrefillCarve c;
   c.scan_bytes = align_up(rat::scan_workspace_bytes(2, B, T, H, Dh));
   c.grid_bytes = align_up((size_t)B * rows * Dh * elt_size(dt));
-  c.all_bytes = W > 0 ? align_up((size_t)B * T * H * Dh * elt_size(dt)) : 0;
-  c.total = c.scan_bytes + 2 * c.grid_bytes + 2 * c.all_bytes;
+  c.allk_bytes = W > 0 ? align_up((size_t)B * T * H * Dh * elt_size(dt)) : 0;
+  c.allv_bytes = W > 0 ? align_up((size_t)B * H * Dh * (bf16 ? prefill_tpad(T) : T) * elt_size(dt)) : 0;
+  c.total = c.scan_bytes + 2 * c.grid_bytes + c.allk_bytes + c.allv_bytes;
   return c;
+}
+
+// Look-back polls before a block recomputes an unpublished predecessor
+// itself.  RAT_SCAN_FALLBACK_SPINS overrides the default (tests force 0 to
+// exercise the recompute path).
+int scan_fallback_spins() {
+  const char* e = std::getenv("RAT_SCAN_FALLBACK_SPINS");
+  return e ? std::atoi(e) : -1;
 }
 
 // Decode split plan: a (b, h) item streams at most ~4096 grid rows per split,
@@ -154,12 +171,13 @@ rat_status_t rat_scan(const void* x, const float* z, const float* h0, void* stat
   p.ten[0].h0 = h0;
   p.ten[0].out_grid = states;
   p.ten[0].h_last = h_last;
+  p.ten[0].grid_mode = rat::kGridToken;
   p.ntensors = 1;
   p.B = B; p.T = T; p.H = H; p.Dh = Dh;
   p.bf16 = dt == RAT_BF16;
-  p.grid_mode = rat::kGridToken;
   p.heads.dil[0] = store_every;
   p.ws = ws;
+  p.fallback_spins = scan_fallback_spins();
   hipError_t e = rat::launch_scan(p, stream);
   if (e != hipSuccess) return fail(RAT_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
   return ok();
@@ -206,19 +224,22 @@ rat_status_t rat_dilated_prefill_stage(rat_prefill_stage_t stage, const void* q,
   void* grid_k = base + cv.scan_bytes;
   void* grid_v = base + cv.scan_bytes + cv.grid_bytes;
   void* all_k = W > 0 ? base + cv.scan_bytes + 2 * cv.grid_bytes : nullptr;
-  void* all_v = W > 0 ? base + cv.scan_bytes + 2 * cv.grid_bytes + cv.all_bytes : nullptr;
+  void* all_v = W > 0 ? base + cv.scan_bytes + 2 * cv.grid_bytes + cv.allk_bytes : nullptr;
+  const bool bf16 = dt == RAT_BF16;
 
   rat::ScanPlan sp;
   std::memset(&sp, 0, sizeof(sp));
   int64_t rows;
-  prefill_grid_layout(T, H, dilation, sp.heads, rows);
-  sp.ten[0] = {k, zk, nullptr, all_k, grid_k, nullptr};
-  sp.ten[1] = {v, zv, nullptr, all_v, grid_v, nullptr};
+  prefill_grid_layout(T, H, dilation, bf16, sp.heads, rows);
+  sp.ten[0] = {k, zk, nullptr, all_k, grid_k, nullptr, rat::kAllToken, rat::kGridHeadRow};
+  sp.ten[1] = {v, zv, nullptr, all_v, grid_v, nullptr, bf16 ? rat::kAllHeadCol : rat::kAllToken,
+               bf16 ? rat::kGridHeadCol : rat::kGridHeadRow};
   sp.ntensors = 2;
   sp.B = B; sp.T = T; sp.H = H; sp.Dh = Dh;
-  sp.bf16 = dt == RAT_BF16;
-  sp.grid_mode = rat::kGridHead;
+  sp.tpad = bf16 ? prefill_tpad(T) : T;
+  sp.bf16 = bf16;
   sp.ws = ws;
+  sp.fallback_spins = scan_fallback_spins();
   if (stage != RAT_STAGE_ATTENTION) {
     hipError_t e = rat::launch_scan(sp, stream);
     if (e != hipSuccess) return fail(RAT_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
@@ -231,6 +252,7 @@ rat_status_t rat_dilated_prefill_stage(rat_prefill_stage_t stage, const void* q,
   ap.grid_k = grid_k; ap.grid_v = grid_v;
   ap.all_k = all_k; ap.all_v = all_v;
   ap.B = B; ap.T = T; ap.H = H; ap.Dh = Dh; ap.W = W;
+  ap.tpad = sp.tpad;
   ap.bf16 = dt == RAT_BF16;
   ap.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)Dh);
   ap.heads = sp.heads;

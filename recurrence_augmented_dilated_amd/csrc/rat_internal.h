@@ -64,38 +64,61 @@ __device__ __forceinline__ int64_t grid_row_offset(const HeadTable& ht, int B, i
 
 // Workspace header (first 256 bytes of every workspace).
 struct WsHeader {
-  uint32_t ticket;   // scan: next chunk ticket (reset each call)
+  uint32_t reserved;
   uint32_t epoch;    // scan: call counter; tags published carries
   uint32_t error;    // sticky bit set: a device-side check failed (see rat.h)
   uint32_t pad[61];
 };
 static_assert(sizeof(WsHeader) == 256, "header size");
 
-constexpr uint32_t kErrScanSpin = 1u;     // look-back wait exceeded its bound
 constexpr uint32_t kErrDecodePos = 2u;    // decode position outside [0, max_pos)
+
+// ---------------------------------------------------------------------------
+// Transposed ("column") state layouts used between the scan and the bf16
+// attention kernel: per (b, h) a [Dh][cap] matrix, keys along a row, cap a
+// multiple of 64.  Inside each 64-key tile of row d, key j is stored at
+//   tile | ((j/8 % 8) ^ (d % 8)) * 8 | ((j/4 % 2) ^ (d/8 % 2)) * 4 | j % 4
+// so that the attention kernel's 8-byte fragment reads (four consecutive
+// keys of sixteen consecutive rows) hit 32 distinct LDS banks.
+// ---------------------------------------------------------------------------
+__host__ __device__ __forceinline__ int64_t col_key_pos(int64_t j, int d) {
+  return (j & ~int64_t(63)) | ((((j >> 3) & 7) ^ (d & 7)) << 3) | ((((j >> 2) & 1) ^ ((d >> 3) & 1)) << 2) |
+         (j & 3);
+}
 
 // ---------------------------------------------------------------------------
 // Launchers (host side, defined in the .hip files)
 // ---------------------------------------------------------------------------
-enum GridMode { kGridToken = 0, kGridHead = 1 };
+enum GridMode {
+  kGridToken = 0,    // [B][T/D][H][Dh], uniform D (public rat_scan layout)
+  kGridHeadRow = 1,  // head h at B*goff[h]*Dh: [B][gcap[h]][Dh]
+  kGridHeadCol = 2   // head h at B*goff[h]*Dh: [B][Dh][gcap[h]], col_key_pos order
+};
+enum AllMode {
+  kAllToken = 0,     // [B][T][H][Dh]
+  kAllHeadCol = 1    // [B][H][Dh][tpad], col_key_pos order, zero past T
+};
 
 struct ScanTensor {
   const void* x;       // [B][T][H][Dh] (f32 or bf16)
   const float* z;      // [B][T][H][Dh]
   const float* h0;     // [B][H][Dh] or null
-  void* out_all;       // [B][T][H][Dh] (input dtype) or null
+  void* out_all;       // all states (input dtype) or null
   void* out_grid;      // grid states (input dtype) or null
   float* h_last;       // [B][H][Dh] or null
+  int all_mode;        // AllMode of out_all
+  int grid_mode;       // GridMode of out_grid
 };
 
 struct ScanPlan {
   ScanTensor ten[2];
   int ntensors;
   int B, T, H, Dh;
+  int64_t tpad;        // row length of kAllHeadCol (multiple of 64, >= T)
   int bf16;            // 1: x and outputs are bf16; 0: fp32
-  int grid_mode;       // kGridToken (uniform D, [B][T/D][H][Dh]) or kGridHead
   HeadTable heads;
   void* ws;            // workspace base (header + look-back arrays)
+  int fallback_spins;  // look-back polls before a local recompute (< 0: default)
 };
 
 size_t scan_workspace_bytes(int ntensors, int B, int T, int H, int Dh);
@@ -104,11 +127,12 @@ hipError_t launch_scan(const ScanPlan& p, hipStream_t s);
 struct AttnPlan {
   const void* q;       // [B][T][H][Dh]
   void* out;           // [B][T][H][Dh]
-  const void* grid_k;  // ragged head-major grid states
-  const void* grid_v;
-  const void* all_k;   // [B][T][H][Dh] states (needed when W > 0)
-  const void* all_v;
+  const void* grid_k;  // grid states, kGridHeadRow
+  const void* grid_v;  // bf16: kGridHeadCol; fp32: kGridHeadRow
+  const void* all_k;   // all states, kAllToken (needed when W > 0)
+  const void* all_v;   // bf16: kAllHeadCol; fp32: kAllToken
   int B, T, H, Dh, W;
+  int64_t tpad;
   int bf16;
   float scale;
   HeadTable heads;

@@ -9,46 +9,47 @@
 // Decomposition.  Channels are contiguous in memory ([B][T][H][Dh]), so a lane
 // owns NC adjacent channels and walks time sequentially; a wave covers 64*NC
 // channels and kLW time steps; a block of kNW waves covers kNW*kLW steps (a
-// "chunk") of one channel slab.  Every element is read once: z (fp32) and x
-// (bf16 or fp32) go to registers, the local scan from a zero carry keeps
-// (h_local, prod g) per step, and the true states follow as
-//     h_t = h_local_t + (prod_{s<=t} g_s) * carry_in
-// once the chunk's carry-in is known.
+// "chunk") of one channel slab.  Every input element is read from HBM once
+// and kept in registers as loaded (bf16/fp32 x, fp32 z): a first pass folds
+// the wave's steps into an aggregate (A = prod g, B = state reached from a
+// zero carry), and once the chunk's carry-in is known a second pass re-runs
+// the recurrence from it over the same registers and stores the states.
+// Recomputing the gates costs VALU work but halves the registers a step
+// needs, which keeps enough waves resident to hide the look-back latency.
 //
-// Carry propagation across chunks is a decoupled look-back: blocks take
-// chunk tickets from an atomic counter (slab fastest), publish their chunk
-// aggregate (A = prod g, B = local end state) right after the local pass,
-// then walk back over predecessors until one has published its inclusive end
-// state.  Each published value is a 64-bit word {epoch:32, float bits:32}
-// written with one relaxed agent-scope atomic store, so a reader validates
-// every word by its tag alone: no fences, no per-call clearing.  A block
-// waits only on lower tickets, which belong to blocks already running, so
-// the waits always end; a bounded spin count still guards them and raises
-// the workspace error flag instead of hanging.
+// Carry propagation across chunks is a decoupled look-back.  Block b of the
+// grid handles chunk b / n_slabs of slab b % n_slabs, publishes its chunk
+// aggregate right after the first pass, then looks back over predecessors
+// (same slab, earlier chunks) until one has published its inclusive end
+// state.  Every thread owns one channel of the slab and reads a window of
+// kWin predecessors per round trip.  Each published value is a 64-bit word
+// {epoch:32, float bits:32} written with one relaxed agent-scope atomic
+// store, so a reader validates every word by its tag alone: no fences, no
+// per-call clearing.  Work is ordered by block index rather than by an
+// atomic ticket (same-address device atomics serialise, about one per
+// 60-70 ns on this part, which capped the scan at a few thousand blocks per
+// 0.3 ms).  Waits cannot deadlock even if blocks were dispatched out of
+// order: a thread that sees no progress from a predecessor for kFallbackSpins
+// polls computes that predecessor's aggregate itself from its inputs and
+// keeps walking back; chunk 0 needs nobody, so every wait ends.
 #include "rat_internal.h"
 
 namespace rat {
 namespace {
 
 constexpr int kLW = 16;              // time steps per wave
-constexpr int kNW = 4;               // waves per block
+constexpr int kNW = 8;               // waves per block
 constexpr int kChunkT = kLW * kNW;   // time steps per block
-constexpr uint32_t kSpinLimit = 1u << 24;
+constexpr int kWin = 2;              // predecessors read per look-back round trip
+constexpr uint32_t kFallbackSpins = 256;   // default polls before computing a predecessor locally
+
+// Hide a register value from the optimiser (an empty asm that "modifies"
+// it), so that pass 2 recomputes the gates instead of keeping pass 1's.
+__device__ __forceinline__ void opaque(uint32_t& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void opaque(float& v) { asm volatile("" : "+v"(v)); }
 
 // Raw vector of NC elements of type XT and its conversions.
 template <typename XT, int NC> struct XVec;
-template <> struct XVec<bf16_t, 4> {
-  using raw = uint2;
-  __device__ static raw load(const bf16_t* p) { return *reinterpret_cast<const uint2*>(p); }
-  __device__ static float get(const raw& r, int c) {
-    const uint32_t w = c < 2 ? r.x : r.y;
-    return (c & 1) ? bf16_hi(w) : bf16_lo(w);
-  }
-  __device__ static void store(bf16_t* p, const float* v) {
-    *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-  }
-  __device__ static raw zero() { return make_uint2(0, 0); }
-};
 template <> struct XVec<bf16_t, 2> {
   using raw = uint32_t;
   __device__ static raw load(const bf16_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
@@ -57,6 +58,7 @@ template <> struct XVec<bf16_t, 2> {
     *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(v[0], v[1]);
   }
   __device__ static raw zero() { return 0u; }
+  __device__ static void hide(raw& r) { opaque(r); }
 };
 template <> struct XVec<bf16_t, 1> {
   using raw = uint32_t;
@@ -66,17 +68,7 @@ template <> struct XVec<bf16_t, 1> {
     *p = bf16_t(pack_bf16x2(v[0], 0.f) & 0xffffu);
   }
   __device__ static raw zero() { return 0u; }
-};
-template <> struct XVec<float, 4> {
-  using raw = float4;
-  __device__ static raw load(const float* p) { return *reinterpret_cast<const float4*>(p); }
-  __device__ static float get(const raw& r, int c) {
-    return c == 0 ? r.x : c == 1 ? r.y : c == 2 ? r.z : r.w;
-  }
-  __device__ static void store(float* p, const float* v) {
-    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-  }
-  __device__ static raw zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ static void hide(raw& r) { opaque(r); }
 };
 template <> struct XVec<float, 2> {
   using raw = float2;
@@ -86,6 +78,7 @@ template <> struct XVec<float, 2> {
     *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
   }
   __device__ static raw zero() { return make_float2(0.f, 0.f); }
+  __device__ static void hide(raw& r) { opaque(r.x); opaque(r.y); }
 };
 template <> struct XVec<float, 1> {
   using raw = float;
@@ -93,18 +86,31 @@ template <> struct XVec<float, 1> {
   __device__ static float get(const raw& r, int) { return r; }
   __device__ static void store(float* p, const float* v) { *p = v[0]; }
   __device__ static raw zero() { return 0.f; }
+  __device__ static void hide(raw& r) { opaque(r); }
 };
+
+// Stores into the transposed (column) layouts: four consecutive keys of one
+// row, or one key.
+__device__ __forceinline__ void store4(bf16_t* p, const float* v) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+}
+__device__ __forceinline__ void store4(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store1(bf16_t* p, float v) { *p = bf16_t(pack_bf16x2(v, 0.f) & 0xffffu); }
+__device__ __forceinline__ void store1(float* p, float v) { *p = v; }
 
 struct ScanArgs {
   ScanTensor ten[2];
   int B, T, H, Dh, C;
-  int grid_mode;
+  int64_t tpad;       // row length of kAllHeadCol outputs
   int n_slabs;        // ntensors * B * slabs_per_bt
   int slabs_per_bt;   // C / (64 * NC)
   uint64_t* agg_a;
   uint64_t* agg_b;
   uint64_t* incl;
   uint32_t* hdr;
+  uint32_t fallback_spins;
   HeadTable heads;
 };
 
@@ -123,25 +129,45 @@ __global__ void scan_prologue(uint32_t* hdr) {
   if (threadIdx.x == 0) {
     uint32_t e = hdr[1] + 1u;
     if (e == 0u) e = 1u;
-    hdr[0] = 0u;   // ticket counter
     hdr[1] = e;    // epoch of this call (hdr[2], the error word, is sticky)
+  }
+}
+
+// Aggregate (prod g, state from a zero carry) of chunk j for one channel,
+// computed straight from the inputs: the look-back's fallback.
+template <typename XT>
+__device__ void chunk_aggregate(const XT* x, const float* z, int64_t C, int T, int j, float& A,
+                                float& Bv) {
+  A = 1.f;
+  Bv = 0.f;
+  const int t_end = min(T, (j + 1) * kChunkT);
+  for (int t = j * kChunkT; t < t_end; ++t) {
+    float g, c;
+    gate_pair(z[(int64_t)t * C], g, c);
+    const float xv = sizeof(XT) == 2 ? bf16_to_f32(reinterpret_cast<const bf16_t*>(x)[(int64_t)t * C])
+                                     : reinterpret_cast<const float*>(x)[(int64_t)t * C];
+    Bv = g * Bv + c * xv;
+    A *= g;
   }
 }
 
 template <typename XT, int NC>
 __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
   using V = XVec<XT, NC>;
+  using Z = XVec<float, NC>;
   constexpr int SC = 64 * NC;   // channels per slab
-  __shared__ uint32_t s_ticket;
-  __shared__ float s_A[kNW][NC][64];
-  __shared__ float s_B[kNW][NC][64];
-  __shared__ float s_carry[kNW][NC][64];
+  static_assert(SC <= kNW * 64, "one look-back thread per channel");
+  __shared__ float s_A[kNW][SC];
+  __shared__ float s_B[kNW][SC];
+  __shared__ float s_carry[kNW][SC];
+  // transposed-output staging: [channel][step] of this chunk (bf16 path)
+  constexpr int kTRow = kChunkT * 2 + 16;   // bytes per channel row (padded)
+  __shared__ __attribute__((aligned(16))) char s_T[sizeof(XT) == 2 ? SC * kTRow : 16];
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  if (threadIdx.x == 0) s_ticket = atomicAdd(&a.hdr[0], 1u);
-  __syncthreads();
-  const uint32_t ticket = s_ticket;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t ticket = blockIdx.x;
   const uint32_t epoch = a.hdr[1];
 
   const int chunk = int(ticket / uint32_t(a.n_slabs));
@@ -151,174 +177,248 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
   const int rem = slab - ti * per_tensor;
   const int b = rem / a.slabs_per_bt;
   const int cs = rem - b * a.slabs_per_bt;
-  const int ch = cs * SC + lane * NC;   // first channel of this lane in [0, C)
-  const int h = ch / a.Dh;
-  const int d = ch - h * a.Dh;
   const ScanTensor tn = ti == 0 ? a.ten[0] : a.ten[1];
   const int64_t C = a.C;
   const int T = a.T;
   const int t0 = chunk * kChunkT + wave * kLW;
+  const int ch = cs * SC + lane * NC;   // first channel of this lane in [0, C)
+  const int h = ch / a.Dh;
+  const int d = ch - h * a.Dh;
 
-  const XT* xp = static_cast<const XT*>(tn.x) + (int64_t)b * T * C + ch;
-  const float* zp = tn.z + (int64_t)b * T * C + ch;
+  // wave-uniform row bases (scalar) plus a small per-lane offset
+  const XT* xbase = static_cast<const XT*>(tn.x) + (int64_t)b * T * C + cs * SC;
+  const float* zbase = tn.z + (int64_t)b * T * C + cs * SC;
+  const int lo = lane * NC;
 
   // ---- load this wave's kLW steps (every element is read exactly once)
   typename V::raw xr[kLW];
-  typename XVec<float, NC>::raw zr[kLW];
+  typename Z::raw zr[kLW];
 #pragma unroll
   for (int s = 0; s < kLW; ++s) {
     const int t = t0 + s;
     if (t < T) {
-      xr[s] = V::load(xp + (int64_t)t * C);
-      zr[s] = XVec<float, NC>::load(zp + (int64_t)t * C);
+      xr[s] = V::load(xbase + (int64_t)t * C + lo);
+      zr[s] = Z::load(zbase + (int64_t)t * C + lo);
     } else {
       xr[s] = V::zero();
-      zr[s] = XVec<float, NC>::zero();
+      zr[s] = Z::zero();
     }
   }
 
-  // ---- local scan from a zero carry
-  float loc[kLW][NC], P[kLW][NC];
-  float hl[NC], pp[NC];
+  // ---- pass 1: aggregate of the wave's steps (identity past the end)
+  {
+    float hl[NC], pp[NC];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) { hl[c] = 0.f; pp[c] = 1.f; }
+    for (int c = 0; c < NC; ++c) { hl[c] = 0.f; pp[c] = 1.f; }
 #pragma unroll
-  for (int s = 0; s < kLW; ++s) {
-    const bool live = (t0 + s) < T;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      float g, cc;
-      gate_pair(XVec<float, NC>::get(zr[s], c), g, cc);
-      if (!live) { g = 1.f; cc = 0.f; }   // identity step past the end
-      hl[c] = g * hl[c] + cc * V::get(xr[s], c);
-      pp[c] *= g;
-      loc[s][c] = hl[c];
-      P[s][c] = pp[c];
-    }
-  }
-#pragma unroll
-  for (int c = 0; c < NC; ++c) { s_A[wave][c][lane] = pp[c]; s_B[wave][c][lane] = hl[c]; }
-  __syncthreads();
-
-  // ---- wave 0: chunk aggregate, look-back, per-wave carries
-  if (wave == 0) {
-    float A[NC], Bv[NC], carry[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      A[c] = 1.f; Bv[c] = 0.f;
-#pragma unroll
-      for (int w = 0; w < kNW; ++w) {
-        const float Aw = s_A[w][c][lane];
-        Bv[c] = Aw * Bv[c] + s_B[w][c][lane];
-        A[c] *= Aw;
-      }
-    }
-    const int64_t widx = (int64_t)ticket * SC + lane * NC;
-    if (chunk == 0) {
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-        carry[c] = tn.h0 ? tn.h0[((int64_t)b * a.H + h) * a.Dh + d + c] : 0.f;
-    } else {
+    for (int s = 0; s < kLW; ++s) {
+      const bool live = (t0 + s) < T;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        publish(a.agg_a + widx + c, tag_word(A[c], epoch));
-        publish(a.agg_b + widx + c, tag_word(Bv[c], epoch));
+        float g, cc;
+        gate_pair(Z::get(zr[s], c), g, cc);
+        if (!live) { g = 1.f; cc = 0.f; }
+        hl[c] = g * hl[c] + cc * V::get(xr[s], c);
+        pp[c] *= g;
       }
-      float accA[NC], accB[NC];
+    }
 #pragma unroll
-      for (int c = 0; c < NC; ++c) { accA[c] = 1.f; accB[c] = 0.f; }
+    for (int c = 0; c < NC; ++c) { s_A[wave][lane * NC + c] = pp[c]; s_B[wave][lane * NC + c] = hl[c]; }
+  }
+  __syncthreads();
+
+  // ---- one thread per channel: chunk aggregate, look-back, per-wave carries
+  if (tid < SC) {
+    const int cl = tid;   // channel within the slab
+    float A = 1.f, Bv = 0.f;
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) {
+      const float Aw = s_A[w][cl];
+      Bv = Aw * Bv + s_B[w][cl];
+      A *= Aw;
+    }
+    const int64_t widx = (int64_t)ticket * SC + cl;
+    float carry;
+    if (chunk == 0) {
+      const int chg = cs * SC + cl;
+      const int hh = chg / a.Dh;
+      carry = tn.h0 ? tn.h0[((int64_t)b * a.H + hh) * a.Dh + (chg - hh * a.Dh)] : 0.f;
+    } else {
+      publish(a.agg_a + widx, tag_word(A, epoch));
+      publish(a.agg_b + widx, tag_word(Bv, epoch));
+      float accA = 1.f, accB = 0.f;
       int j = chunk - 1;
       uint32_t spins = 0;
       bool done = false;
       while (!done) {
-        const int64_t pidx = ((int64_t)j * a.n_slabs + slab) * SC + lane * NC;
-        uint64_t wi[NC];
-        bool ok = true;
+        uint64_t wi[kWin], wa[kWin], wb[kWin];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          wi[c] = peek(a.incl + pidx + c);
-          ok = ok && uint32_t(wi[c] >> 32) == epoch;
-        }
-        if (ok) {
-#pragma unroll
-          for (int c = 0; c < NC; ++c) carry[c] = accA[c] * word_value(wi[c]) + accB[c];
-          done = true;
-        } else {
-          uint64_t wa[NC], wb[NC];
-          bool ok2 = true;
-#pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            wa[c] = peek(a.agg_a + pidx + c);
-            wb[c] = peek(a.agg_b + pidx + c);
-            ok2 = ok2 && uint32_t(wa[c] >> 32) == epoch && uint32_t(wb[c] >> 32) == epoch;
-          }
-          if (ok2) {
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-              accB[c] = accA[c] * word_value(wb[c]) + accB[c];
-              accA[c] *= word_value(wa[c]);
-            }
-            --j;
-          } else if (++spins > kSpinLimit) {
-            atomicOr(&a.hdr[2], kErrScanSpin);
-#pragma unroll
-            for (int c = 0; c < NC; ++c) carry[c] = 0.f;
-            done = true;
+        for (int i = 0; i < kWin; ++i) {
+          const int jj = j - i;
+          if (jj >= 0) {
+            const int64_t pidx = ((int64_t)jj * a.n_slabs + slab) * SC + cl;
+            wi[i] = peek(a.incl + pidx);
+            wa[i] = peek(a.agg_a + pidx);
+            wb[i] = peek(a.agg_b + pidx);
           } else {
-            __builtin_amdgcn_s_sleep(1);
+            wi[i] = wa[i] = wb[i] = 0;
           }
+        }
+        int used = 0;
+        bool stop = false;
+#pragma unroll
+        for (int i = 0; i < kWin; ++i) {
+          if (!stop && !done) {
+            if (uint32_t(wi[i] >> 32) == epoch) {
+              carry = accA * word_value(wi[i]) + accB;
+              done = true;
+            } else if (uint32_t(wa[i] >> 32) == epoch && uint32_t(wb[i] >> 32) == epoch) {
+              accB = accA * word_value(wb[i]) + accB;
+              accA *= word_value(wa[i]);
+              ++used;
+            } else {
+              stop = true;
+            }
+          }
+        }
+        if (done) break;
+        j -= used;
+        if (used > 0) {
+          spins = 0;
+        } else if (++spins > a.fallback_spins) {
+          // predecessor j shows no progress: fold its chunk in directly
+          const int chg = cs * SC + cl;
+          float Aj, Bj;
+          chunk_aggregate<XT>(static_cast<const XT*>(tn.x) + (int64_t)b * T * C + chg,
+                              tn.z + (int64_t)b * T * C + chg, C, T, j, Aj, Bj);
+          accB = accA * Bj + accB;
+          accA *= Aj;
+          if (j == 0) {
+            const int hh = chg / a.Dh;
+            const float h0v = tn.h0 ? tn.h0[((int64_t)b * a.H + hh) * a.Dh + (chg - hh * a.Dh)] : 0.f;
+            carry = accA * h0v + accB;
+            done = true;
+          }
+          --j;
+          spins = 0;
+        } else {
+          __builtin_amdgcn_s_sleep(2);
         }
       }
     }
+    publish(a.incl + widx, tag_word(A * carry + Bv, epoch));
+    float cw = carry;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) publish(a.incl + widx + c, tag_word(A[c] * carry[c] + Bv[c], epoch));
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      float cw = carry[c];
-#pragma unroll
-      for (int w = 0; w < kNW; ++w) {
-        s_carry[w][c][lane] = cw;
-        cw = s_A[w][c][lane] * cw + s_B[w][c][lane];
-      }
+    for (int w = 0; w < kNW; ++w) {
+      s_carry[w][cl] = cw;
+      cw = s_A[w][cl] * cw + s_B[w][cl];
     }
   }
   __syncthreads();
 
-  // ---- finalize: true states, stores
-  float cin[NC];
+  // ---- pass 2: the recurrence from the carry-in; stores
 #pragma unroll
-  for (int c = 0; c < NC; ++c) cin[c] = s_carry[wave][c][lane];
+  for (int s = 0; s < kLW; ++s) { V::hide(xr[s]); Z::hide(zr[s]); }
+  float hv[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) hv[c] = s_carry[wave][lane * NC + c];
 
-  const int D = a.grid_mode == kGridToken ? a.heads.dil[0] : a.heads.dil[h];
+  const int D = tn.grid_mode == kGridToken ? a.heads.dil[0] : a.heads.dil[h];
   // first grid position >= t0: smallest j >= t0 with (j + 1) % D == 0
   int next_grid = (t0 / D) * D + (D - 1);
   if (next_grid < t0) next_grid += D;
   XT* out_all = static_cast<XT*>(tn.out_all);
   XT* out_grid = static_cast<XT*>(tn.out_grid);
-  const int64_t G_tok = D > 0 ? T / D : 0;
+  const int64_t G_tok = T / D;
+  const bool tok_all = out_all && tn.all_mode == kAllToken;
+  const bool col_all = out_all && tn.all_mode == kAllHeadCol;
+  const bool col_grid = out_grid && tn.grid_mode == kGridHeadCol;
+  // per-channel row bases of the column layouts
+  const int64_t col_all_row = (((int64_t)b * a.H + h) * a.Dh + d) * a.tpad;
+  const int64_t col_grid_row = col_grid ? grid_row_offset(a.heads, a.B, b, h, 0, a.Dh) +
+                                              (int64_t)d * a.heads.gcap[h] : 0;
+  float run[NC][4];
 
 #pragma unroll
   for (int s = 0; s < kLW; ++s) {
     const int t = t0 + s;
     if (t < T) {
-      float hv[NC];
 #pragma unroll
-      for (int c = 0; c < NC; ++c) hv[c] = loc[s][c] + P[s][c] * cin[c];
-      if (out_all) V::store(out_all + ((int64_t)b * T + t) * C + ch, hv);
+      for (int c = 0; c < NC; ++c) {
+        float g, cc;
+        gate_pair(Z::get(zr[s], c), g, cc);
+        hv[c] = g * hv[c] + cc * V::get(xr[s], c);
+      }
+      if (tok_all) V::store(out_all + ((int64_t)b * T + t) * C + cs * SC + lo, hv);
       if (out_grid && t == next_grid) {
         const int64_t i = (t + 1) / D - 1;
-        int64_t off;
-        if (a.grid_mode == kGridToken)
-          off = (((int64_t)b * G_tok + i) * a.H + h) * a.Dh + d;
-        else
-          off = grid_row_offset(a.heads, a.B, b, h, i, a.Dh) + d;
-        V::store(out_grid + off, hv);
+        if (tn.grid_mode == kGridToken) {
+          V::store(out_grid + (((int64_t)b * G_tok + i) * a.H + h) * a.Dh + d, hv);
+        } else if (tn.grid_mode == kGridHeadRow) {
+          V::store(out_grid + grid_row_offset(a.heads, a.B, b, h, i, a.Dh) + d, hv);
+        } else {
+#pragma unroll
+          for (int c = 0; c < NC; ++c)
+            store1(out_grid + col_grid_row + (int64_t)c * a.heads.gcap[h] + col_key_pos(i, d + c), hv[c]);
+        }
         next_grid += D;
       }
       if (tn.h_last && t == T - 1) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) tn.h_last[((int64_t)b * a.H + h) * a.Dh + d + c] = hv[c];
       }
+    }
+    if (col_all) {
+      // keys t-3..t of each channel; positions past T are written as zeros
+#pragma unroll
+      for (int c = 0; c < NC; ++c) run[c][s & 3] = t < T ? hv[c] : 0.f;
+      if ((s & 3) == 3) {
+        if constexpr (sizeof(XT) == 2) {
+          // stage in LDS; written out row by row below
+#pragma unroll
+          for (int c = 0; c < NC; ++c)
+            store4(reinterpret_cast<bf16_t*>(s_T + (lane * NC + c) * kTRow) + wave * kLW + (s - 3), run[c]);
+        } else if (t - 3 < a.tpad) {
+#pragma unroll
+          for (int c = 0; c < NC; ++c)
+            store4(out_all + col_all_row + (int64_t)c * a.tpad + col_key_pos(t - 3, d + c), run[c]);
+        }
+      }
+    }
+  }
+  if constexpr (sizeof(XT) == 2) {
+    if (col_all) {
+      // Write the chunk's [channel][128 keys] block into the transposed rows
+      // with 16-byte stores.  In col_key_pos order the physical 8-key chunk p
+      // of a 64-key tile holds logical chunk p ^ (d % 8), its two 4-key halves
+      // swapped when (d / 8) % 2 == 1.
+      __syncthreads();
+      const int64_t key0 = (int64_t)chunk * kChunkT;
+      constexpr int CPR = kChunkT / 8;   // 16-byte chunks per channel row
+#pragma unroll
+      for (int k = 0; k < SC * CPR / (kNW * 64); ++k) {
+        const int task = tid + kNW * 64 * k;
+        const int r = task / CPR;          // channel within the slab
+        const int p = task - r * CPR;      // physical chunk within the 128 keys
+        const int chg = cs * SC + r;
+        const int hh = chg / a.Dh;
+        const int dd = chg - hh * a.Dh;
+        const int lc = (p & ~7) | ((p & 7) ^ (dd & 7));
+        uint4 w = *reinterpret_cast<const uint4*>(s_T + r * kTRow + lc * 16);
+        if ((dd >> 3) & 1) w = make_uint4(w.z, w.w, w.x, w.y);
+        const int64_t kpos = key0 + p * 8;
+        if (kpos < a.tpad)
+          *reinterpret_cast<uint4*>(out_all + (((int64_t)b * a.H + hh) * a.Dh + dd) * a.tpad + kpos) = w;
+      }
+    }
+  }
+  // the wave holding position T-1 zero-fills the column grid past its last entry
+  if (col_grid && t0 <= T - 1 && T - 1 < t0 + kLW) {
+    const int cap = a.heads.gcap[h];
+    for (int i = T / D; i < cap; ++i) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        store1(out_grid + col_grid_row + (int64_t)c * cap + col_key_pos(i, d + c), 0.f);
     }
   }
 }
@@ -330,8 +430,10 @@ hipError_t launch_typed(const ScanArgs& a, int n_chunks, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Channels per lane.  Two (128-channel slabs) measured best on MI355X: twice
+// as many independent carry chains as four, each with half the chunks in
+// flight, at equal coalescing (256-byte rows of x per wave load).
 int pick_nc(int C) {
-  if (C % 256 == 0) return 4;
   if (C % 128 == 0) return 2;
   return 1;
 }
@@ -351,8 +453,9 @@ hipError_t launch_scan(const ScanPlan& p, hipStream_t s) {
   a.ten[0] = p.ten[0];
   a.ten[1] = p.ntensors > 1 ? p.ten[1] : p.ten[0];
   a.B = p.B; a.T = p.T; a.H = p.H; a.Dh = p.Dh; a.C = p.H * p.Dh;
-  a.grid_mode = p.grid_mode;
+  a.tpad = p.tpad;
   a.heads = p.heads;
+  a.fallback_spins = p.fallback_spins >= 0 ? uint32_t(p.fallback_spins) : kFallbackSpins;
   const int nc = pick_nc(a.C);
   a.slabs_per_bt = a.C / (64 * nc);
   a.n_slabs = p.ntensors * p.B * a.slabs_per_bt;
@@ -368,14 +471,8 @@ hipError_t launch_scan(const ScanPlan& p, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nch = int(n_chunks);
-  if (p.bf16) {
-    if (nc == 4) return launch_typed<bf16_t, 4>(a, nch, s);
-    if (nc == 2) return launch_typed<bf16_t, 2>(a, nch, s);
-    return launch_typed<bf16_t, 1>(a, nch, s);
-  }
-  if (nc == 4) return launch_typed<float, 4>(a, nch, s);
-  if (nc == 2) return launch_typed<float, 2>(a, nch, s);
-  return launch_typed<float, 1>(a, nch, s);
+  if (p.bf16) return nc == 2 ? launch_typed<bf16_t, 2>(a, nch, s) : launch_typed<bf16_t, 1>(a, nch, s);
+  return nc == 2 ? launch_typed<float, 2>(a, nch, s) : launch_typed<float, 1>(a, nch, s);
 }
 
 }  // namespace rat

@@ -106,3 +106,24 @@ def test_scan_empty_and_tiny():
     assert s.shape[1] == 0
     states, h_last, ref = _run(1, 1, 2, 64, torch.float32, 1, seed=7)
     _check_states(states, ref, 1, torch.float32, "scan T=1")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_scan_lookback_recompute_path(dtype, monkeypatch):
+    """Force the look-back's fallback (a block that sees no published
+    predecessor folds that chunk in from its inputs) on every wait."""
+    monkeypatch.setenv("RAT_SCAN_FALLBACK_SPINS", "0")
+    states, h_last, ref = _run(2, 3000, 2, 128, dtype, 1, seed=41)
+    _check_states(states, ref, 1, dtype, f"scan fallback {dtype}")
+    assert np.max(np.abs(f64(h_last) - ref[:, -1])) <= 1e-5
+
+
+def test_prefill_with_lookback_recompute_path(monkeypatch):
+    R = need_gpu()
+    monkeypatch.setenv("RAT_SCAN_FALLBACK_SPINS", "0")
+    x = inputs.prefill_inputs(1, 2000, 2, 128, dtype=torch.bfloat16, seed=42)
+    d = {k: v.to("cuda:0") for k, v in x.items()}
+    out = R.rat_dilated_prefill(d["q"], d["k"], d["v"], d["zk"], d["zv"], 16, 32)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["zk"]), f64(x["zv"]), 16, 32)
+    assert report("prefill fallback", f64(out), ref) <= 2e-2
