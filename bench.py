@@ -218,6 +218,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--config", type=int, default=0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration) and exit")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -225,6 +227,17 @@ def main():
         sys.exit(2)
 
     import torch
+    if a.calibrate_copy:
+        n = (1 << 30) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        ms = time_loop(lambda: dst.copy_(src), 5, torch)
+        print(json.dumps({"calibration": "copy", "bytes_read": n * 4, "bytes_written": n * 4, "ms": ms,
+                          "GBps_read_plus_write": 2 * n * 4 / (ms * 1e-3) / 1e9}), flush=True)
+        return
     import recurrence_augmented_dilated_amd as R
     from recurrence_augmented_dilated_amd import inputs
     R.lib()
