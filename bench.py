@@ -41,6 +41,35 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "recurrence_augmented_dilated_amd", "csrc")
+KERNEL_SOURCES = {"scan": ["scan.hip", "rat_internal.h"], "attention": ["prefill_attn.hip", "rat_internal.h"],
+                  "decode": ["decode.hip", "rat_internal.h"]}
+
+
+def source_hash(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload_key):
+    """HBM bytes per launch from a committed rocprofv3 counter profile, or None
+    if there is none for this kernel/workload or the kernel source changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload_key}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        prof = json.load(fh)
+    if prof.get("source_sha256") != source_hash(kernel):
+        return None
+    return prof.get("hbm_bytes_per_dispatch")
+
+
 # ---------------------------------------------------------------------------
 # work model (algorithmic bytes and flops; counts from the key-set ranges)
 # ---------------------------------------------------------------------------
@@ -184,17 +213,18 @@ def bench_decode(c, steps, warmup, torch, R, inputs):
 # CPU baseline: the fp64 oracle as it stands, one thread
 # ---------------------------------------------------------------------------
 
-def cpu_baseline_prefill(c, x, torch):
-    import numpy as np
+def cpu_baseline_prefill(c, x, torch, heads):
+    """The fp64 oracle on `heads` of the workload's heads (every query row, the
+    full-length recurrence), one thread; tokens/s scaled by H / len(heads)."""
+    import contextlib
     import oracle
     try:
         from threadpoolctl import threadpool_limits
     except ImportError:  # pragma: no cover
         threadpool_limits = None
     f = lambda t: t.float().cpu().double().numpy()  # noqa: E731
-    hs = [0, 1]   # sample: two heads, every query row, full-length recurrence
+    hs = list(range(heads))
     xs = {k: f(v[:, :, hs]) for k, v in x.items()}
-    import contextlib
     lim = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
     with lim:
         t0 = time.perf_counter()
@@ -203,8 +233,18 @@ def cpu_baseline_prefill(c, x, torch):
     full = sec * c["H"] / len(hs)
     tok_s = c["B"] * c["T"] / full
     return dict(value=tok_s, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"oracle prefill of heads {hs} of {c['H']} (all {c['T']} rows, full recurrence) "
-                       f"in {sec:.1f} s on 1 thread; scaled by H/2 to the whole workload")
+                sample=f"fp64 oracle prefill of {len(hs)} of {c['H']} heads (all {c['T']} query rows and the "
+                       f"full recurrence) took {sec:.1f} s on 1 thread; tokens/s scaled by H/{len(hs)}")
+
+
+def measure_copy(torch):
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ms = time_loop(lambda: dst.copy_(src), 5, torch)
+    del src, dst
+    return 2 * n * 4 / (ms * 1e-3) / 1e9
 
 
 # ---------------------------------------------------------------------------
@@ -217,6 +257,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=4, help="heads the CPU-baseline oracle run covers")
     ap.add_argument("--config", type=int, default=0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
@@ -265,6 +306,7 @@ def main():
         }
         dom = "scan" if p["ms_scan"] >= p["ms_attn"] else "attention"
         k = kernels[dom]
+        wkey = f"prefill_T{c['T']}_D{c['D']}_W{c['W']}"
         result.update({
             "value": tok_s, "steps": a.steps, "warmup": a.warmup, "ms_per_step": p["ms"],
             "dtype": c["dtype"],
@@ -272,10 +314,13 @@ def main():
                                    f"W={c['W']} {c['dtype']}", "config_id": cfg_id, "B": c["B"], "T": c["T"],
                        "heads": c["H"], "head_dim": c["Dh"], "dilation": c["D"], "window": c["W"]},
             "roofline": {"kernel": dom, "bound": k["bound"], "achieved": k["achieved"], "peak": k["peak"],
-                         "unit": k["unit"], "frac": k["frac"], "traffic": None},
+                         "unit": k["unit"], "frac": k["frac"], "traffic": measured_traffic(dom, wkey)},
             "kernels": kernels,
             "ws_error": p["ws_error"],
+            "copy_GBps_measured": measure_copy(torch),
         })
+        for name in kernels:
+            kernels[name]["traffic"] = measured_traffic(name, wkey)
         if not a.no_decode and a.config == 0:
             cd = CONFIGS[4]
             d = bench_decode(cd, a.decode_steps, 8, torch, R, inputs)
@@ -287,7 +332,7 @@ def main():
                              "frac": gbs / PEAK_HBM}, "ws_error": d["ws_error"]}
         if not a.no_cpu_baseline:
             log("[bench] cpu baseline (oracle) ...")
-            result["cpu_baseline"] = cpu_baseline_prefill(c, p["x"], torch)
+            result["cpu_baseline"] = cpu_baseline_prefill(c, p["x"], torch, min(a.cpu_heads, c["H"]))
     else:
         d = bench_decode(c, a.decode_steps, 8, torch, R, inputs)
         gbs = d["bytes_per_step"] / (d["ms"] * 1e-3)
@@ -297,7 +342,8 @@ def main():
             "config": {"workload": f"decode B={c['B']} H={c['H']} Dh={c['Dh']} ctx={c['ctx']} "
                                    f"W={c['W']} dilation={sorted(set(c['D']))}", "config_id": cfg_id},
             "roofline": {"kernel": "decode", "bound": "hbm", "achieved": gbs / 1e9, "peak": PEAK_HBM / 1e9,
-                         "unit": "GB/s", "frac": gbs / PEAK_HBM, "traffic": None},
+                         "unit": "GB/s", "frac": gbs / PEAK_HBM,
+                         "traffic": measured_traffic("decode", f"decode_config{cfg_id}")},
             "ws_error": d["ws_error"],
         })
     print(json.dumps(result), flush=True)

@@ -127,14 +127,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
   constexpr int VL = VBYTES / 1024 / kWaves;
   static_assert(KL >= 1 && VL >= 1 && KL * kWaves * 1024 == KBYTES && VL * kWaves * 1024 == VBYTES, "tiles");
 
-  // three-stage ring: tile it is read from stage it % 3 while tiles it+1 and
-  // it+2 are in flight into the other two
-  __shared__ __attribute__((aligned(1024))) char sK0[KBYTES];
-  __shared__ __attribute__((aligned(1024))) char sK1[KBYTES];
-  __shared__ __attribute__((aligned(1024))) char sK2[KBYTES];
-  __shared__ __attribute__((aligned(1024))) char sV0[VBYTES];
-  __shared__ __attribute__((aligned(1024))) char sV1[VBYTES];
-  __shared__ __attribute__((aligned(1024))) char sV2[VBYTES];
+  // Four-stage ring: while tile it is consumed, tiles it+1..it+3 are landing
+  // or in flight.
+  __shared__ __attribute__((aligned(1024))) char sK[4][KBYTES];
+  __shared__ __attribute__((aligned(1024))) char sV[4][VBYTES];
 
   int b, h, qtile;
   block_coords(blockIdx.x, a.B, a.H, a.n_qtiles, b, h, qtile);
@@ -185,7 +181,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
   const bf16_t* avt = W > 0 ? static_cast<const bf16_t*>(a.all_v) + ((int64_t)b * H + h) * DH * a.tpad : nullptr;
 
   // issue the direct loads of tile `it` into (dK, dV)
-  auto issue = [&](int it, char* dK, char* dV) {
+  auto issue = [&](int it, char* dK, char* dV) __attribute__((always_inline)) {
     const bf16_t* kb;
     const bf16_t* vb;
     int64_t kstride, vstride;
@@ -204,7 +200,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
       const int j = wave * KL + u;                 // 1 KB slice of the tile
       const int r = j * (64 / LPR) + lane / LPR;   // key row
       const int p = lane % LPR;                    // physical 16-byte chunk
-      const int c = p ^ (r & 7);                   // logical chunk stored there
+      const int c = p ^ (r & (LPR - 1) & 15);      // logical chunk stored there
       load_lds16(kb + (int64_t)(row0 + min(r, nvalid - 1)) * kstride + 8 * c, dK + j * 1024);
     }
 #pragma unroll
@@ -223,10 +219,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  auto compute = [&](int it, const char* cK, const char* cV) {
-    const bool is_grid = it < ntile_g;
-    bool needed, masked;
-    int kbase;   // grid index or position of the tile's first key
+  // needed: does any query of this wave see a key of tile it?
+  // masked: does some (query, key) pair of the tile fall outside the key set?
+  auto tile_info = [&](int it, bool& is_grid, bool& needed, bool& masked, int& kbase) __attribute__((always_inline)) {
+    is_grid = it < ntile_g;
     if (is_grid) {
       kbase = it * kBN;
       needed = wave_live && kbase < ng_w1;
@@ -236,33 +232,54 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
       needed = wave_live && kbase <= tw1 && kbase + kBN - 1 >= max(0, tw0 - W + 1);
       masked = !(kbase >= tw1 - W + 1 && kbase + kBN - 1 <= tw0);
     }
-    if (!needed) return;
+  };
 
-    // ---- S^T = K Q^T for two 32-key blocks
-    floatx16_t s[2];
+  // S^T = K Q^T of one tile into sc (two 32-key blocks)
+  auto scores = [&](const char* cK, floatx16_t* sc) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int m = 32 * kb + n;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int c = (2 * ks + g) ^ (m & 7);
+        const int c = (2 * ks + g) ^ (m & (LPR - 1) & 15);
         const uint4 w = *reinterpret_cast<const uint4*>(cK + m * KROW + 16 * c);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), qf[ks], s[kb], 0, 0, 0);
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), qf[ks], sc[kb], 0, 0, 0);
       }
     }
+  };
 
-    // ---- mask
+  // mask, online softmax and O^T += V^T P^T for the scores s of tile it
+  auto finish = [&](int it, const char* cV, floatx16_t* s) __attribute__((always_inline)) {
+    bool is_grid, needed, masked;
+    int kbase;
+    tile_info(it, is_grid, needed, masked, kbase);
+    if (!needed) return;
+    // ---- mask: key index kbase + c(kb, r) + 4g, branch-free selects
     if (masked) {
+      if (is_grid) {
+        // valid while the grid index is below this query's count
+        const int thr = ng_me - kbase - 4 * g;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = kbase + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool ok = is_grid ? j < ng_me : (j >= win_lo_me && j <= tq);
-          if (!ok) s[kb][r] = -INFINITY;
-        }
+          for (int r = 0; r < 16; ++r) {
+            const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
+            s[kb][r] = c < thr ? s[kb][r] : -INFINITY;
+          }
+      } else {
+        // valid inside [max(0, t-W+1), t]: one unsigned range compare
+        const int lo = win_lo_me - kbase - 4 * g;
+        const uint32_t span = uint32_t(tq - win_lo_me);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
+            s[kb][r] = uint32_t(c - lo) <= span ? s[kb][r] : -INFINITY;
+          }
+      }
     }
 
     // ---- online softmax (base 2; running max shared by the two lane halves)
@@ -319,37 +336,36 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
   };
 
   constexpr int LPW = KL + VL;   // direct loads per wave per tile
-  // one pipeline step: prefetch tile it+2, consume tile it, make tile it+1 visible
-  // The stage pointers are __restrict__ so that, once inlined, the direct
-  // loads into (nK, nV) and the reads of (cK, cV) carry disjoint alias
-  // scopes and the compiler need not wait for the in-flight tile before
-  // reading the current one.
-  auto step = [&](int it, const char* __restrict__ cK, const char* __restrict__ cV, char* __restrict__ nK,
-                  char* __restrict__ nV) {
-    const bool pre = it + 2 < ntiles;
-    if (pre) issue(it + 2, nK, nV);
-    compute(it, cK, cV);
-    if (pre) wait_vmcnt<LPW>();   // tile it+1 has landed; tile it+2 may fly
+  constexpr int kAhead = 3;      // tiles in flight ahead of the one consumed
+  floatx16_t sc[2];
+  auto step = [&](int it) __attribute__((always_inline)) {
+    const bool pre = it + kAhead < ntiles;
+    if (pre) issue(it + kAhead, sK[(it + kAhead) & 3], sV[(it + kAhead) & 3]);
+    bool is_grid, needed, masked;
+    int kbase;
+    tile_info(it, is_grid, needed, masked, kbase);
+    if (needed) {
+      scores(sK[it & 3], sc);
+      finish(it, sV[it & 3], sc);
+    }
+    // tile it+1 must have landed; later tiles may still fly
+    const int later = min(ntiles - 1, it + kAhead) - (it + 1);
+    if (later >= 2) wait_vmcnt<2 * LPW>();
+    else if (later == 1) wait_vmcnt<LPW>();
     else wait_vmcnt<0>();
     ring_barrier();
   };
 
   wait_vmcnt<0>();   // Q fragments are in registers before the ring starts
+  for (int p = 0; p < kAhead && p < ntiles; ++p) issue(p, sK[p], sV[p]);
   if (ntiles > 0) {
-    issue(0, sK0, sV0);
-    if (ntiles > 1) {
-      issue(1, sK1, sV1);
-      wait_vmcnt<LPW>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    const int later = min(ntiles, kAhead) - 1;   // tiles issued after tile 0
+    if (later >= 2) wait_vmcnt<2 * LPW>();
+    else if (later == 1) wait_vmcnt<LPW>();
+    else wait_vmcnt<0>();
     ring_barrier();
   }
-  for (int it = 0; it < ntiles; it += 3) {
-    step(it, sK0, sV0, sK2, sV2);
-    if (it + 1 < ntiles) step(it + 1, sK1, sV1, sK0, sV0);
-    if (it + 2 < ntiles) step(it + 2, sK2, sV2, sK1, sV1);
-  }
+  for (int it = 0; it < ntiles; ++it) step(it);
 
   // ---- normalise and store (empty key set -> zeros)
   const float l_tot = l_run + __shfl_xor(l_run, 32);
