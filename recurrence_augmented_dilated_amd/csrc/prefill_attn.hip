@@ -17,15 +17,16 @@
 // gfx950-native kernel: a q-tile walks the compact grid tiles (only the tile
 // holding the n_g boundary is masked) and then the window band.
 //
-// bf16 kernel.  Block = 4 waves x 32 queries.  Per 64-key tile each wave
+// bf16 kernel.  Block = 8 waves x 32 queries.  Per 64-key tile each wave
 // computes S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys on M, queries on N),
 // so that after the online softmax its fp32 accumulators, converted to bf16,
 // are already the B operand of O^T = V^T P^T: no shuffles between the two
-// products.  K is staged row-major in LDS (rows padded to 272 B, conflict-free
-// 16-byte fragment reads); V is transposed while staged (key pairs packed into
-// dwords, XOR-swizzled columns) so that V^T fragments are two 8-byte LDS
-// reads.  Softmax runs in base 2 with the scale folded into one FMA.  Block
-// order is heaviest q-tile first and keeps each (b, h) pair on one XCD.
+// products.  Tiles stream through a four-stage LDS ring filled by direct
+// global->LDS loads: K rows with XOR-swizzled 16-byte chunks, V from the
+// scan's transposed layout, where one lane's eight keys of a 16-key step are
+// a single 16-byte chunk.  Softmax runs in base 2 with the scale folded into
+// one FMA and tree reductions.  Block order is heaviest q-tile first and
+// keeps each (b, h) pair on one XCD.
 //
 // fp32 kernel.  A plain exact-fp32 path (one or two lanes per query, keys
 // staged in LDS) for fp32 inputs.
@@ -83,6 +84,41 @@ __device__ __forceinline__ void block_coords(int bid, int B, int H, int n_qtiles
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel
 // ---------------------------------------------------------------------------
+
+// v_permlane32_swap with both operands v: afterwards every lane holds the
+// value of its column's lower-half lane (lane & 31) in lo and of its upper-half
+// lane (lane | 32) in hi, without an LDS round trip.
+__device__ __forceinline__ void half_pair(float v, float& lo, float& hi) {
+  const uint32_t u = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+
+// Max and sum of a lane's 32 scores as balanced trees (short dependency
+// chains; the order of the fp32 sum differs from a left-to-right loop only
+// by rounding).
+__device__ __forceinline__ float tree_max32(const floatx16_t* s) {
+  float m[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) m[r] = fmaxf(s[0][r], s[1][r]);
+#pragma unroll
+  for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+    for (int r = 0; r < w; ++r) m[r] = fmaxf(m[r], m[r + w]);
+  return m[0];
+}
+__device__ __forceinline__ float tree_sum32(const floatx16_t* s) {
+  float m[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) m[r] = s[0][r] + s[1][r];
+#pragma unroll
+  for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+    for (int r = 0; r < w; ++r) m[r] += m[r + w];
+  return m[0];
+}
+
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void gbl_void_t;
 
@@ -283,12 +319,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
     }
 
     // ---- online softmax (base 2; running max shared by the two lane halves)
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    float mx, mx_lo, mx_hi;
+    half_pair(tree_max32(s), mx_lo, mx_hi);
+    mx = fmaxf(mx_lo, mx_hi);
     const float m_new = fmaxf(m_run, mx * a.sl2);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     // rescale only when some row of the wave raised its running max
@@ -301,16 +334,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
         for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
     }
     m_run = m_new;
-    float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], a.sl2, -m_use));
-        s[kb][r] = p;
-        psum += p;
-      }
-    l_run += psum;
+      for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], a.sl2, -m_use));
+    l_run += tree_sum32(s);
 
     // ---- O^T += V^T P^T over four 16-key steps
 #pragma unroll
@@ -326,10 +354,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int d = 32 * db + n;
-        const char* row = cV + d * (kBN * 2);
-        const uint2 lo = *reinterpret_cast<const uint2*>(row + 2 * col_key_pos(16 * st + 4 * g, d));
-        const uint2 hi = *reinterpret_cast<const uint2*>(row + 2 * col_key_pos(16 * st + 8 + 4 * g, d));
-        const uint4 vw = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        // keys 16st + 4g + {0..3} and 16st + 8 + 4g + {0..3}: one 16-byte chunk
+        const uint4 vw = *reinterpret_cast<const uint4*>(cV + d * (kBN * 2) + 16 * ((2 * st + g) ^ col_swz(d)));
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vw), pf, o[db], 0, 0, 0);
       }
     }
@@ -368,7 +394,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
   for (int it = 0; it < ntiles; ++it) step(it);
 
   // ---- normalise and store (empty key set -> zeros)
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  float l_lo, l_hi;
+  half_pair(l_run, l_lo, l_hi);
+  const float l_tot = l_lo + l_hi;
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   if (q_live) {
     bf16_t* op = static_cast<bf16_t*>(a.out) + ((int64_t)b * T + tq) * rowC + h * DH;

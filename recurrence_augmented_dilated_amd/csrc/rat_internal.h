@@ -76,18 +76,18 @@ constexpr uint32_t kErrDecodePos = 2u;    // decode position outside [0, max_pos
 // ---------------------------------------------------------------------------
 // Transposed ("column") state layouts used between the scan and the bf16
 // attention kernel: per (b, h) a [Dh][cap] matrix, keys along a row, cap a
-// multiple of 64.  Inside each 64-key tile of row d, key j is stored at
-//   tile | ((j/8 % 8) ^ col_chunk_xor(d)) * 8 | ((j/4 % 2) ^ col_half_xor(d)) * 4 | j % 4.
-// The attention kernel reads four consecutive keys (8 bytes) of 32
-// consecutive rows per instruction; with 128-byte rows these land in
-// distinct banks both for a 32-bank LDS (16 lanes per cycle) and a 64-bank
-// LDS (32 lanes per cycle).
+// multiple of 64.  Inside each 64-key tile of row d the keys sit in eight
+// 16-byte chunks: logical chunk c = 2 * (j/16 % 4) + (j/4 % 2) holds keys
+// 16s + 4g + {0..3} then 16s + 8 + 4g + {0..3} (s = c/2, g = c%2), which is
+// the bf16 operand one MFMA lane needs for a 16-key step, and it is stored
+// at physical chunk c ^ col_swz(d).  With 128-byte rows, the 16 lanes that
+// read chunk c of 16 consecutive rows hit distinct banks both for a 32-bank
+// LDS (8 lanes per cycle) and a 64-bank LDS (16 lanes per cycle).
 // ---------------------------------------------------------------------------
-__host__ __device__ __forceinline__ int col_chunk_xor(int d) { return (d & 7) ^ ((d >> 4) & 1); }
-__host__ __device__ __forceinline__ int col_half_xor(int d) { return (d >> 3) & 1; }
+__host__ __device__ __forceinline__ int col_swz(int d) { return (d ^ (d >> 3)) & 7; }
+__host__ __device__ __forceinline__ int col_chunk(int64_t j) { return int(((j >> 3) & 6) | ((j >> 2) & 1)); }
 __host__ __device__ __forceinline__ int64_t col_key_pos(int64_t j, int d) {
-  return (j & ~int64_t(63)) | ((((j >> 3) & 7) ^ col_chunk_xor(d)) << 3) |
-         ((((j >> 2) & 1) ^ col_half_xor(d)) << 2) | (j & 3);
+  return (j & ~int64_t(63)) | ((col_chunk(j) ^ col_swz(d)) << 3) | (((j >> 3) & 1) << 2) | (j & 3);
 }
 
 // ---------------------------------------------------------------------------

@@ -390,8 +390,8 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
     if (col_all) {
       // Write the chunk's [channel][128 keys] block into the transposed rows
       // with 16-byte stores.  In col_key_pos order the physical 8-key chunk p
-      // of a 64-key tile holds logical chunk p ^ col_chunk_xor(d), its two
-      // 4-key halves swapped when col_half_xor(d) is set.
+      // of a 64-key tile holds logical chunk c = p ^ col_swz(d): keys
+      // 16(c/2) + 4(c%2) + {0..3} and the four keys 8 further on.
       __syncthreads();
       const int64_t key0 = (int64_t)chunk * kChunkT;
       constexpr int CPR = kChunkT / 8;   // 16-byte chunks per channel row
@@ -403,9 +403,11 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
         const int chg = cs * SC + r;
         const int hh = chg / a.Dh;
         const int dd = chg - hh * a.Dh;
-        const int lc = (p & ~7) | ((p & 7) ^ col_chunk_xor(dd));
-        uint4 w = *reinterpret_cast<const uint4*>(s_T + r * kTRow + lc * 16);
-        if (col_half_xor(dd)) w = make_uint4(w.z, w.w, w.x, w.y);
+        const int lc = (p & 7) ^ col_swz(dd);
+        const int k0 = 64 * (p >> 3) + 16 * (lc >> 1) + 4 * (lc & 1);   // first key, natural order
+        const uint2 w0 = *reinterpret_cast<const uint2*>(s_T + r * kTRow + 2 * k0);
+        const uint2 w1 = *reinterpret_cast<const uint2*>(s_T + r * kTRow + 2 * (k0 + 8));
+        const uint4 w = make_uint4(w0.x, w0.y, w1.x, w1.y);
         const int64_t kpos = key0 + p * 8;
         if (kpos < a.tpad)
           *reinterpret_cast<uint4*>(out_all + (((int64_t)b * a.H + hh) * a.Dh + dd) * a.tpad + kpos) = w;
