@@ -141,28 +141,41 @@ def bench_prefill(c, steps, warmup, torch, R, inputs):
     def step():
         R.rat_dilated_prefill(*args, out=out, ws=ws)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ms = time_loop(step, steps, torch)
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / steps * 1e3
-    log(f"[bench] prefill {ms:.3f} ms/step (wall {wall:.3f})")
-
-    # per-stage timing (same kernels, launched stage by stage)
     def scan_only():
         R.rat_dilated_prefill_stage(1, *args, out=out, ws=ws)
 
     def attn_only():
         R.rat_dilated_prefill_stage(2, *args, out=out, ws=ws)
 
-    scan_only()
-    ms_scan = time_loop(scan_only, steps, torch)
-    ms_attn = time_loop(attn_only, steps, torch)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # single-call API (both kernels behind one rat_dilated_prefill call)
+    ms_call = time_loop(step, steps, torch)
+
+    # Timed region: the same two launches issued stage by stage, with HIP
+    # events between them on the stream they run on, so each kernel's
+    # duration is measured inside the region that gives the step time.
+    s = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(s)
+        scan_only()
+        ev[i][1].record(s)
+        attn_only()
+        ev[i][2].record(s)
+    ev[-1][2].synchronize()
+    wall = (time.perf_counter() - t0) / steps * 1e3
+    ms = ev[0][0].elapsed_time(ev[-1][2]) / steps
+    ms_scan = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    ms_attn = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
     err = R.workspace_error(ws)
-    log(f"[bench] stages: scan {ms_scan:.3f} ms, attention {ms_attn:.3f} ms, ws error {err}")
-    return dict(ms=ms, wall_ms=wall, ms_scan=ms_scan, ms_attn=ms_attn, x=x, out=out, ws_error=err)
+    log(f"[bench] prefill {ms:.3f} ms/step (wall {wall:.3f}; single call {ms_call:.3f}); "
+        f"scan {ms_scan:.3f} ms, attention {ms_attn:.3f} ms per launch; ws error {err}")
+    return dict(ms=ms, ms_call=ms_call, wall_ms=wall, ms_scan=ms_scan, ms_attn=ms_attn, x=x, out=out,
+                ws_error=err)
 
 
 def bench_decode(c, steps, warmup, torch, R, inputs):
@@ -249,6 +262,95 @@ def measure_copy(torch):
 
 # ---------------------------------------------------------------------------
 
+# ---------------------------------------------------------------------------
+# offline: rocprofv3 CSV output -> short summaries under profiles/ (CPU only)
+# ---------------------------------------------------------------------------
+
+KERNEL_PATTERNS = {"scan": "scan_kernel", "attention": "attn_bf16_kernel", "decode": "decode_kernel"}
+COPY_BYTES = 1 << 30   # --calibrate-copy: bytes read and bytes written by one copy
+
+
+def _find_csv(d, suffix):
+    import glob
+    hits = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not hits:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return hits[0]
+
+
+def _counter_rows(d, counter):
+    import csv
+    rows = []
+    with open(_find_csv(d, "counter_collection.csv")) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def summarize_pmc(kernel, workload, fetch_dir, write_dir, cfetch_dir, cwrite_dir, bench_args):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of `kernel`, scaled by what
+    the same counters read for a plain copy of known size, into
+    profiles/<kernel>_<workload>_pmc.json (+ .txt)."""
+    pat = KERNEL_PATTERNS[kernel]
+    fetch = [v for n, v in _counter_rows(fetch_dir, "FETCH_SIZE") if pat in n]
+    write = [v for n, v in _counter_rows(write_dir, "WRITE_SIZE") if pat in n]
+    # the calibration run's largest dispatch is the 1 GiB copy
+    cf = max(v for _, v in _counter_rows(cfetch_dir, "FETCH_SIZE"))
+    cw = max(v for _, v in _counter_rows(cwrite_dir, "WRITE_SIZE"))
+    f_fetch = COPY_BYTES / (cf * 1024.0)
+    f_write = COPY_BYTES / (cw * 1024.0)
+    fk = sum(fetch) / len(fetch)
+    wk = sum(write) / len(write)
+    hbm = fk * 1024.0 * f_fetch + wk * 1024.0 * f_write
+    cmds = [f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o pmc -- python3 bench.py {bench_args}",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o pmc -- python3 bench.py {bench_args}",
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {cfetch_dir} -o pmc -- python3 bench.py --calibrate-copy",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {cwrite_dir} -o pmc -- python3 bench.py --calibrate-copy",
+            f"python3 bench.py --summarize-pmc {kernel} {workload} {fetch_dir} {write_dir} {cfetch_dir} {cwrite_dir} "
+            f"--pmc-bench-args '{bench_args}'"]
+    out = {"kernel": kernel, "kernel_name_pattern": pat, "workload": workload, "source_sha256": source_hash(kernel),
+           "dispatches": [len(fetch), len(write)], "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
+           "copy_fetch_kib": cf, "copy_write_kib": cw, "factor_fetch": f_fetch, "factor_write": f_write,
+           "hbm_bytes_per_dispatch": hbm, "commands": cmds}
+    base = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc")
+    with open(base + ".json", "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    with open(base + ".txt", "w") as fh:
+        fh.write(f"HBM traffic of {kernel} ({pat}) on workload {workload}\n\n")
+        fh.write("\n".join("$ " + c for c in cmds) + "\n\n")
+        fh.write(f"dispatches averaged: FETCH {len(fetch)}, WRITE {len(write)}\n")
+        fh.write(f"FETCH_SIZE {fk:.1f} KiB/dispatch x {f_fetch:.3f} (1 GiB copy read {cf:.1f} KiB)\n")
+        fh.write(f"WRITE_SIZE {wk:.1f} KiB/dispatch x {f_write:.3f} (1 GiB copy wrote {cw:.1f} KiB)\n")
+        fh.write(f"HBM bytes per dispatch: {hbm:.4g}\n")
+        fh.write(f"source sha256 of the kernel's files: {out['source_sha256']}\n")
+    print(json.dumps(out))
+
+
+def summarize_trace(trace_dir, kernel, workload, bench_args):
+    """Launch statistics of `kernel` from a --kernel-trace --stats run into
+    profiles/<kernel>_<workload>_kernel_trace.txt."""
+    import csv
+    path = _find_csv(trace_dir, "kernel_stats.csv")
+    pat = KERNEL_PATTERNS[kernel]
+    with open(path) as fh:
+        rows = [r for r in csv.DictReader(fh) if pat in r["Name"]]
+    lines = [f"rocprofv3 kernel statistics of {kernel} ({pat}) on workload {workload}", "",
+             f"$ rocprofv3 --kernel-trace --stats --output-format csv -d {trace_dir} -o kt -- python3 bench.py "
+             f"{bench_args}",
+             f"$ python3 bench.py --summarize-trace {trace_dir} {kernel} {workload} --pmc-bench-args '{bench_args}'",
+             ""]
+    for r in rows:
+        lines += [f"kernel: {r['Name']}",
+                  f"calls {int(float(r['Calls']))}, average {float(r['AverageNs']) / 1e3:.2f} us, "
+                  f"min {float(r['MinNs']) / 1e3:.2f} us, max {float(r['MaxNs']) / 1e3:.2f} us, "
+                  f"{float(r['Percentage']):.2f}% of the run's kernel time"]
+    with open(os.path.join(ROOT, "profiles", f"{kernel}_{workload}_kernel_trace.txt"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -257,11 +359,24 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=4, help="heads the CPU-baseline oracle run covers")
+    ap.add_argument("--cpu-heads", type=int, default=16, help="heads the CPU-baseline oracle run covers")
     ap.add_argument("--config", type=int, default=0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--summarize-pmc", nargs=6, metavar=("KERNEL", "WORKLOAD", "FETCH_DIR", "WRITE_DIR",
+                                                         "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="offline: write profiles/<KERNEL>_<WORKLOAD>_pmc.json from rocprofv3 counter CSVs")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_DIR", "KERNEL", "WORKLOAD"),
+                    help="offline: write profiles/<KERNEL>_<WORKLOAD>_kernel_trace.txt from a "
+                         "--kernel-trace --stats run")
+    ap.add_argument("--pmc-bench-args", default="", help="bench.py arguments of the profiled run (recorded)")
     a = ap.parse_args()
+    if a.summarize_pmc:
+        summarize_pmc(*a.summarize_pmc, a.pmc_bench_args)
+        return
+    if a.summarize_trace:
+        summarize_trace(*a.summarize_trace, a.pmc_bench_args)
+        return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(see DESIGN.md for how the operator would shard).", file=sys.stderr)
@@ -309,6 +424,7 @@ def main():
         wkey = f"prefill_T{c['T']}_D{c['D']}_W{c['W']}"
         result.update({
             "value": tok_s, "steps": a.steps, "warmup": a.warmup, "ms_per_step": p["ms"],
+            "single_call_ms_per_step": p["ms_call"],
             "dtype": c["dtype"],
             "config": {"workload": f"prefill B={c['B']} H={c['H']} Dh={c['Dh']} T={c['T']} D={c['D']} "
                                    f"W={c['W']} {c['dtype']}", "config_id": cfg_id, "B": c["B"], "T": c["T"],
@@ -328,8 +444,10 @@ def main():
             result["decode"] = {
                 "workload": "decode B=256 H=16 Dh=128 ctx=32768 D=16 W=64 bf16", "steps": d["steps"],
                 "tokens_per_s": cd["B"] / (d["ms"] * 1e-3), "ms_per_step": d["ms"],
-                "roofline": {"bound": "hbm", "achieved": gbs / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                             "frac": gbs / PEAK_HBM}, "ws_error": d["ws_error"]}
+                "roofline": {"kernel": "decode", "bound": "hbm", "achieved": gbs / 1e9, "peak": PEAK_HBM / 1e9,
+                             "unit": "GB/s", "frac": gbs / PEAK_HBM,
+                             "traffic": measured_traffic("decode", "decode_config4")},
+                "ws_error": d["ws_error"]}
         if not a.no_cpu_baseline:
             log("[bench] cpu baseline (oracle) ...")
             result["cpu_baseline"] = cpu_baseline_prefill(c, p["x"], torch, min(a.cpu_heads, c["H"]))
