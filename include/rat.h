@@ -151,6 +151,48 @@ rat_status_t rat_grid_layout(int32_t H, const int32_t* dilation, int64_t max_pos
                              int64_t* grid_off, int32_t* grid_cap, int64_t* rows);
 
 /* ------------------------------------------------------------------------ *
+ * rat_prefill_chunk -- prefill positions p0 .. p0+T-1 of sequences whose
+ * positions 0 .. p0-1 are held in a decode cache, and extend that cache to
+ * positions 0 .. p0+T-1 (the prefill-then-decode serving of RAT+ Fig. 2;
+ * key sets as in the abstract and Fig. 1c, with the grid at absolute
+ * positions).  With p0 = 0 and zero states it is a prefill that leaves the
+ * decode cache behind; a sequence split into chunks gets the outputs of one
+ * call over the whole sequence, up to the fp32 rounding of the state
+ * carried between chunks.
+ *
+ *   q, k, v, zk, zv, out  as rat_dilated_prefill, for the T rows of the
+ *                         chunk (row t is position p0 + t)
+ *   state_k/_v   [B][H][Dh] fp32, in/out: the state after position p0-1
+ *                (zeros when p0 = 0) -> the state after position p0+T-1
+ *   grid_k/_v    ragged grid caches (layout of rat_grid_layout), dtype,
+ *                in/out: entries of positions before p0 are read, entries
+ *                of positions p0 .. p0+T-1 written
+ *   grid_off, grid_cap  host [H]: their layout; grid_cap[h] >= max_pos / D_h
+ *   ring_k/_v    [B][H][W][Dh] dtype, in/out (NULL allowed when W = 0): the
+ *                slots of positions p0-W+1 .. p0-1 are read, the slots of
+ *                the chunk's last min(W, T) positions written
+ *   p0           first position of the chunk, the same for every sequence;
+ *                a multiple of 64
+ *   max_pos      cache capacity in positions; p0 + T <= max_pos < 2^31
+ *   dilation, W, scale  as rat_dilated_prefill (W is the ring length)
+ *   ws           workspace of at least rat_prefill_chunk_workspace_size(...)
+ *                bytes (scratch only: nothing in it is read by a later call)
+ * Errors: p0 not a multiple of 64 -> RAT_ERR_UNSUPPORTED; p0 < 0,
+ * p0 + T > max_pos or a grid capacity below max_pos / D_h ->
+ * RAT_ERR_INVALID_ARG.  T = 0 is a no-op (buffers may then be NULL).
+ * ------------------------------------------------------------------------ */
+size_t rat_prefill_chunk_workspace_size(int32_t B, int32_t T, int32_t H, int32_t Dh,
+                                        const int32_t* dilation, int32_t W, int64_t p0,
+                                        rat_dtype_t dtype);
+rat_status_t rat_prefill_chunk(const void* q, const void* k, const void* v, const float* zk,
+                               const float* zv, void* out, float* state_k, float* state_v,
+                               void* grid_k, void* grid_v, const int64_t* grid_off,
+                               const int32_t* grid_cap, void* ring_k, void* ring_v, int64_t p0,
+                               int64_t max_pos, int32_t B, int32_t T, int32_t H, int32_t Dh,
+                               const int32_t* dilation, int32_t W, float scale, rat_dtype_t dtype,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
  * rat_decode_step -- one new token per sequence (RAT+ Fig. 2: step update of
  * the recurrence, attention over the cached states; abstract: the grid
  * cache is D times smaller than a dense cache).

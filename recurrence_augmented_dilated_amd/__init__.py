@@ -77,6 +77,12 @@ def lib():
             L.rat_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                           c_i64, vp, c_int, c_int, c_int, vp, c_int, c_f, c_int,
                                           vp, c_sz, vp]
+            L.rat_prefill_chunk_workspace_size.restype = c_sz
+            L.rat_prefill_chunk_workspace_size.argtypes = [c_int, c_int, c_int, c_int, vp, c_int, c_i64, c_int]
+            L.rat_prefill_chunk.restype = c_int
+            L.rat_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, c_i64,
+                                            c_i64, c_int, c_int, c_int, c_int, vp, c_int, c_f, c_int, vp,
+                                            c_sz, vp]
             _lib = L
     return _lib
 
@@ -250,6 +256,38 @@ def rat_decode_step(q, k, v, zk, zv, state_k, state_v, grid_k, grid_v, grid_off,
     _check(lib().rat_decode_step(
         _ptr(q), _ptr(k), _ptr(v), _ptr(zk), _ptr(zv), _ptr(state_k), _ptr(state_v), _ptr(grid_k),
         _ptr(grid_v), off, cap, _ptr(ring_k), _ptr(ring_v), _ptr(pos), int(max_pos), _ptr(out), B, H,
+        Dh, _i32_array(dil), int(W), s, _dtype_code(q), _ptr(ws), ws.numel(), _stream(q.device)))
+    return out
+
+
+def rat_prefill_chunk_workspace_size(B, T, H, Dh, dilation, W, p0, dtype=torch.bfloat16) -> int:
+    d = _i32_array(_per_head(dilation, H))
+    code = RAT_BF16 if dtype == torch.bfloat16 else RAT_F32
+    return int(lib().rat_prefill_chunk_workspace_size(B, T, H, Dh, d, W, int(p0), code))
+
+
+def rat_prefill_chunk(q, k, v, zk, zv, state_k, state_v, grid_k, grid_v, grid_off, grid_cap,
+                      ring_k, ring_v, p0, max_pos, dilation, W, scale=None, out=None, ws=None):
+    """Prefill positions p0 .. p0+T-1 continuing a decode cache (mutates the
+    states, grid and ring caches); returns out [B, T, H, Dh]."""
+    B, T, H, Dh = q.shape
+    for t in (k, v):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v must share shape and dtype")
+    for t in (zk, zv):
+        if t.shape != q.shape or t.dtype != torch.float32:
+            raise ValueError("zk, zv must be fp32 with q's shape")
+    dil = _per_head(dilation, H)
+    if out is None:
+        out = torch.empty_like(q)
+    if ws is None:
+        ws = workspace(rat_prefill_chunk_workspace_size(B, T, H, Dh, dil, W, p0, q.dtype), q.device, "chunk")
+    off = (ctypes.c_int64 * H)(*[int(x) for x in grid_off])
+    cap = _i32_array(grid_cap)
+    s = -1.0 if scale is None else float(scale)
+    _check(lib().rat_prefill_chunk(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(zk), _ptr(zv), _ptr(out), _ptr(state_k), _ptr(state_v),
+        _ptr(grid_k), _ptr(grid_v), off, cap, _ptr(ring_k), _ptr(ring_v), int(p0), int(max_pos), B, T, H,
         Dh, _i32_array(dil), int(W), s, _dtype_code(q), _ptr(ws), ws.numel(), _stream(q.device)))
     return out
 

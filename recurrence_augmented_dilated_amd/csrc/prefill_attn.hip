@@ -48,10 +48,16 @@ struct AttnArgs {
   const void* all_v;
   int B, T, H, W;
   int64_t tpad;               // row length of the transposed all-states V
+  int p0;                     // absolute position of query row 0
+  int base;                   // absolute position of all-state row 0 (multiple of 64)
+  int64_t arows;              // rows of the token-layout all-state buffers
   int n_qtiles;
   float sl2;                  // softmax scale * log2(e)
-  HeadTable heads;
+  HeadTable heads;            // dilation; grid keys at goff / gcap
+  int64_t vgoff[kMaxHeads];   // grid values: element offset B * vgoff[h] * Dh
+  int32_t vgcap[kMaxHeads];   // grid values: capacity (row length in kGridHeadCol)
 };
+static_assert(sizeof(AttnArgs) <= 4096, "kernel argument size");
 
 __device__ __forceinline__ int n_grid(int t, int W, int D) {
   const int x = t - W + 1;
@@ -179,10 +185,13 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
   const int D = a.heads.dil[h];
   const int64_t rowC = (int64_t)H * DH;   // elements between tokens
 
+  // query rows are relative to the call, key positions absolute (p0 + row)
+  const int P0 = a.p0;
   const int t0 = qtile * kBM;
   const int t_last = min(t0 + kBM, T) - 1;
-  const int tq = t0 + wave * 32 + n;      // this lane's query (column of S^T)
+  const int tq = t0 + wave * 32 + n;      // this lane's query row (column of S^T)
   const bool q_live = tq < T;
+  const int tqa = P0 + tq;                // its absolute position
 
   // Q^T fragments (B operand): query tq, head dims 16*ks + 8*g .. +7
   bf16x8_t qf[KS];
@@ -196,24 +205,24 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
   }
 
   // key ranges of the block (window tiles start on a 64-key boundary)
-  const int ng_hi = n_grid(t_last, W, D);
-  const int ng_me = q_live ? n_grid(tq, W, D) : 0;
+  const int ng_hi = n_grid(P0 + t_last, W, D);
+  const int ng_me = q_live ? n_grid(tqa, W, D) : 0;
   const int ntile_g = (ng_hi + kBN - 1) / kBN;
-  const int j_lo = W > 0 ? max(0, t0 - W + 1) / kBN * kBN : 0;
-  const int ntile_w = W > 0 ? (t_last - j_lo) / kBN + 1 : 0;
+  const int j_lo = W > 0 ? max(a.base, P0 + t0 - W + 1) / kBN * kBN : 0;
+  const int ntile_w = W > 0 ? (P0 + t_last - j_lo) / kBN + 1 : 0;
   const int ntiles = ntile_g + ntile_w;
-  const int win_lo_me = max(0, tq - W + 1);
-  // this wave's query range: tiles that are fully masked for it are skipped
-  const int tw0 = t0 + wave * 32;
-  const int tw1 = min(tw0 + 31, T - 1);
-  const bool wave_live = tw0 < T;
+  const int win_lo_me = max(0, tqa - W + 1);
+  // this wave's queries (absolute): tiles that are fully masked for it are skipped
+  const int tw0 = P0 + t0 + wave * 32;
+  const int tw1 = P0 + min(t0 + wave * 32 + 31, T - 1);
+  const bool wave_live = t0 + wave * 32 < T;
   const int ng_w0 = wave_live ? n_grid(tw0, W, D) : 0;
   const int ng_w1 = wave_live ? n_grid(tw1, W, D) : 0;
 
-  const int cap = a.heads.gcap[h];
+  const int cap = a.vgcap[h];             // row length of the transposed grid values
   const bf16_t* gk = static_cast<const bf16_t*>(a.grid_k) + grid_row_offset(a.heads, a.B, b, h, 0, DH);
-  const bf16_t* gvt = static_cast<const bf16_t*>(a.grid_v) + grid_row_offset(a.heads, a.B, b, h, 0, DH);
-  const bf16_t* ak = W > 0 ? static_cast<const bf16_t*>(a.all_k) + (int64_t)b * T * rowC + h * DH : nullptr;
+  const bf16_t* gvt = static_cast<const bf16_t*>(a.grid_v) + ((int64_t)a.B * a.vgoff[h] + (int64_t)b * cap) * DH;
+  const bf16_t* ak = W > 0 ? static_cast<const bf16_t*>(a.all_k) + (int64_t)b * a.arows * rowC + h * DH : nullptr;
   const bf16_t* avt = W > 0 ? static_cast<const bf16_t*>(a.all_v) + ((int64_t)b * H + h) * DH * a.tpad : nullptr;
 
   // issue the direct loads of tile `it` into (dK, dV)
@@ -227,8 +236,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
       kb = gk; kstride = DH; nvalid = ng_hi - row0;
       vb = gvt; vstride = cap;
     } else {
-      row0 = j_lo + (it - ntile_g) * kBN;
-      kb = ak; kstride = rowC; nvalid = t_last + 1 - row0;
+      row0 = j_lo + (it - ntile_g) * kBN - a.base;   // buffer row of the tile
+      kb = ak; kstride = rowC; nvalid = P0 + t_last + 1 - (row0 + a.base);
       vb = avt; vstride = a.tpad;
     }
 #pragma unroll
@@ -307,7 +316,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
       } else {
         // valid inside [max(0, t-W+1), t]: one unsigned range compare
         const int lo = win_lo_me - kbase - 4 * g;
-        const uint32_t span = uint32_t(tq - win_lo_me);
+        const uint32_t span = uint32_t(tqa - win_lo_me);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -432,10 +441,12 @@ __global__ __launch_bounds__(64 * (DH / 64)) void attn_f32_kernel(const AttnArgs
   const int T = a.T, H = a.H, W = a.W;
   const int D = a.heads.dil[h];
   const int64_t rowC = (int64_t)H * DH;
+  const int P0 = a.p0;
   const int t0 = qtile * 64;
   const int t_last = min(t0 + 64, T) - 1;
-  const int tq = t0 + qi;
+  const int tq = t0 + qi;                 // query row; absolute position P0 + tq
   const bool q_live = tq < T;
+  const int tqa = P0 + tq;
 
   float q[64], acc[64];
   {
@@ -448,16 +459,16 @@ __global__ __launch_bounds__(64 * (DH / 64)) void attn_f32_kernel(const AttnArgs
 #pragma unroll
     for (int i = 0; i < 64; ++i) acc[i] = 0.f;
   }
-  const int ng_hi = n_grid(t_last, W, D);
-  const int ng_me = q_live ? n_grid(tq, W, D) : 0;
+  const int ng_hi = n_grid(P0 + t_last, W, D);
+  const int ng_me = q_live ? n_grid(tqa, W, D) : 0;
   const int ntile_g = (ng_hi + kF32Keys - 1) / kF32Keys;
-  const int j_lo = W > 0 ? max(0, t0 - W + 1) : 0;
-  const int ntile_w = W > 0 ? (t_last - j_lo + kF32Keys) / kF32Keys : 0;
-  const int win_lo_me = max(0, tq - W + 1);
+  const int j_lo = W > 0 ? max(a.base, P0 + t0 - W + 1) : 0;   // absolute
+  const int ntile_w = W > 0 ? (P0 + t_last - j_lo + kF32Keys) / kF32Keys : 0;
+  const int win_lo_me = max(0, tqa - W + 1);
   const float* gk = static_cast<const float*>(a.grid_k) + grid_row_offset(a.heads, a.B, b, h, 0, DH);
-  const float* gv = static_cast<const float*>(a.grid_v) + grid_row_offset(a.heads, a.B, b, h, 0, DH);
-  const float* ak = W > 0 ? static_cast<const float*>(a.all_k) + (int64_t)b * T * rowC + h * DH : nullptr;
-  const float* av = W > 0 ? static_cast<const float*>(a.all_v) + (int64_t)b * T * rowC + h * DH : nullptr;
+  const float* gv = static_cast<const float*>(a.grid_v) + ((int64_t)a.B * a.vgoff[h] + (int64_t)b * a.vgcap[h]) * DH;
+  const float* ak = W > 0 ? static_cast<const float*>(a.all_k) + (int64_t)b * a.arows * rowC + h * DH : nullptr;
+  const float* av = W > 0 ? static_cast<const float*>(a.all_v) + (int64_t)b * a.arows * rowC + h * DH : nullptr;
 
   float m_run = -INFINITY, l_run = 0.f;
   for (int it = 0; it < ntile_g + ntile_w; ++it) {
@@ -469,7 +480,9 @@ __global__ __launch_bounds__(64 * (DH / 64)) void attn_f32_kernel(const AttnArgs
     if (is_grid) {
       kb = gk; vb = gv; stride = DH; row0 = it * kF32Keys; nvalid = ng_hi - row0;
     } else {
-      kb = ak; vb = av; stride = rowC; row0 = j_lo + (it - ntile_g) * kF32Keys; nvalid = t_last + 1 - row0;
+      // buffer row of the tile (absolute position - base)
+      kb = ak; vb = av; stride = rowC; row0 = j_lo + (it - ntile_g) * kF32Keys - a.base;
+      nvalid = P0 + t_last + 1 - (row0 + a.base);
     }
     __syncthreads();
     for (int e = tid * 4; e < kF32Keys * DH; e += NT * 4) {
@@ -489,8 +502,8 @@ __global__ __launch_bounds__(64 * (DH / 64)) void attn_f32_kernel(const AttnArgs
       if (is_grid) {
         valid = row0 + kk < ng_me;
       } else {
-        const int j = row0 + kk;
-        valid = j >= win_lo_me && j <= tq && kk < nvalid;
+        const int j = row0 + a.base + kk;   // absolute position of the key
+        valid = j >= win_lo_me && j <= tqa && kk < nvalid;
       }
       float sp = 0.f;
 #pragma unroll
@@ -532,8 +545,15 @@ hipError_t launch_prefill_attention(const AttnPlan& p, hipStream_t s) {
   a.all_k = p.all_k; a.all_v = p.all_v;
   a.B = p.B; a.T = p.T; a.H = p.H; a.W = p.W;
   a.tpad = p.tpad;
+  a.p0 = (int)p.p0;
+  a.base = (int)p.base;
+  a.arows = p.arows > 0 ? p.arows : p.T;
   a.sl2 = p.scale * 1.4426950408889634f;
   a.heads = p.heads;
+  for (int h = 0; h < kMaxHeads; ++h) {
+    a.vgoff[h] = p.vgoff[h];
+    a.vgcap[h] = p.vgcap[h];
+  }
   const int BH = p.B * p.H;
   if (p.bf16) {
     a.n_qtiles = (p.T + kBM - 1) / kBM;

@@ -124,6 +124,51 @@ void decode_splits(int32_t B, int32_t H, const int32_t* dilation, int32_t W, int
   (void)W;
 }
 
+// Chunked prefill (positions p0 .. p0+T-1 continuing a decode cache).
+// All-state buffers start at absolute position base = max(0, p0 - Wpre),
+// Wpre = W - 1 rounded up to 64, so that every window of the chunk's
+// queries lies inside them and their tiles stay 64-aligned; rows
+// [0, p0 - base) come from the ring.  The bf16 path also keeps the grid
+// values every chunk query can see transposed, per head rounded up to 64.
+struct ChunkCarve {
+  size_t scan_bytes, h0_bytes, allk_bytes, allv_bytes, vcol_bytes, total;
+  int64_t base, all_row0, arows, tpad;
+  int64_t vgoff[RAT_MAX_HEADS];
+  int32_t vgcap[RAT_MAX_HEADS], rows[RAT_MAX_HEADS];
+};
+
+int64_t grid_seen(int64_t t_last, int32_t W, int32_t D) {
+  const int64_t x = t_last - W + 1;   // grid entries of query t_last: max(0, t-W+1) / D
+  return x > 0 ? x / D : 0;
+}
+
+ChunkCarve chunk_carve(int32_t B, int32_t T, int32_t H, int32_t Dh, const int32_t* dilation, int32_t W,
+                       int64_t p0, rat_dtype_t dt) {
+  ChunkCarve c;
+  std::memset(&c, 0, sizeof(c));
+  const bool bf16 = dt == RAT_BF16;
+  const size_t e = elt_size(dt);
+  const int64_t wpre = W > 0 ? ((int64_t)W - 1 + 63) / 64 * 64 : 0;
+  c.base = std::max<int64_t>(0, p0 - wpre);
+  c.all_row0 = p0 - c.base;
+  c.arows = c.all_row0 + T;
+  c.tpad = (c.arows + 63) / 64 * 64;
+  c.scan_bytes = align_up(rat::scan_workspace_bytes(2, B, T, H, Dh));
+  c.h0_bytes = align_up((size_t)2 * B * H * Dh * sizeof(float));
+  c.allk_bytes = W > 0 ? align_up((size_t)B * c.arows * H * Dh * e) : 0;
+  c.allv_bytes = W > 0 ? align_up((size_t)B * H * Dh * (bf16 ? c.tpad : c.arows) * e) : 0;
+  int64_t acc = 0;
+  for (int h = 0; h < H; ++h) {
+    c.rows[h] = (int32_t)grid_seen(p0 + T - 1, W, dilation[h]);
+    c.vgcap[h] = bf16 ? (c.rows[h] + 63) / 64 * 64 : 0;
+    c.vgoff[h] = acc;
+    acc += c.vgcap[h];
+  }
+  c.vcol_bytes = bf16 ? align_up((size_t)B * acc * Dh * 2) : 0;
+  c.total = c.scan_bytes + c.h0_bytes + c.allk_bytes + c.allv_bytes + c.vcol_bytes;
+  return c;
+}
+
 }  // namespace
 
 extern "C" {
@@ -237,6 +282,7 @@ rat_status_t rat_dilated_prefill_stage(rat_prefill_stage_t stage, const void* q,
   sp.ntensors = 2;
   sp.B = B; sp.T = T; sp.H = H; sp.Dh = Dh;
   sp.tpad = bf16 ? prefill_tpad(T) : T;
+  sp.arows = T;
   sp.bf16 = bf16;
   sp.ws = ws;
   sp.fallback_spins = scan_fallback_spins();
@@ -253,10 +299,161 @@ rat_status_t rat_dilated_prefill_stage(rat_prefill_stage_t stage, const void* q,
   ap.all_k = all_k; ap.all_v = all_v;
   ap.B = B; ap.T = T; ap.H = H; ap.Dh = Dh; ap.W = W;
   ap.tpad = sp.tpad;
+  ap.arows = T;
   ap.bf16 = dt == RAT_BF16;
   ap.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)Dh);
   ap.heads = sp.heads;
+  for (int h = 0; h < H; ++h) {
+    ap.vgoff[h] = sp.heads.goff[h];
+    ap.vgcap[h] = sp.heads.gcap[h];
+  }
   hipError_t e = rat::launch_prefill_attention(ap, stream);
+  if (e != hipSuccess) return fail(RAT_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+size_t rat_prefill_chunk_workspace_size(int32_t B, int32_t T, int32_t H, int32_t Dh,
+                                        const int32_t* dilation, int32_t W, int64_t p0,
+                                        rat_dtype_t dt) {
+  if (check_common(B, T, H, Dh, dt) != RAT_OK || W < 0 || p0 < 0 || check_dilation(dilation, H) != RAT_OK)
+    return 0;
+  return chunk_carve(B, T, H, Dh, dilation, W, p0, dt).total;
+}
+
+rat_status_t rat_prefill_chunk(const void* q, const void* k, const void* v, const float* zk,
+                               const float* zv, void* out, float* state_k, float* state_v,
+                               void* grid_k, void* grid_v, const int64_t* grid_off,
+                               const int32_t* grid_cap, void* ring_k, void* ring_v, int64_t p0,
+                               int64_t max_pos, int32_t B, int32_t T, int32_t H, int32_t Dh,
+                               const int32_t* dilation, int32_t W, float scale, rat_dtype_t dt,
+                               void* ws, size_t ws_bytes, hipStream_t stream) {
+  rat_status_t st = check_common(B, T, H, Dh, dt);
+  if (st != RAT_OK) return st;
+  if (W < 0) return fail(RAT_ERR_INVALID_ARG, "W must be >= 0 (got %d)", W);
+  if ((st = check_dilation(dilation, H)) != RAT_OK) return st;
+  if (p0 < 0) return fail(RAT_ERR_INVALID_ARG, "p0 must be >= 0 (got %lld)", (long long)p0);
+  if (p0 % 64 != 0) return fail(RAT_ERR_UNSUPPORTED, "p0 must be a multiple of 64 (got %lld)", (long long)p0);
+  if (max_pos < 1 || max_pos > INT32_MAX)
+    return fail(RAT_ERR_INVALID_ARG, "max_pos must be in [1, 2^31) (got %lld)", (long long)max_pos);
+  if (p0 + T > max_pos)
+    return fail(RAT_ERR_INVALID_ARG, "p0 + T = %lld exceeds max_pos = %lld", (long long)(p0 + T),
+                (long long)max_pos);
+  if (!grid_off || !grid_cap) return fail(RAT_ERR_INVALID_ARG, "grid_off and grid_cap must not be NULL");
+  bool any_grid = false;
+  for (int h = 0; h < H; ++h) {
+    if (grid_off[h] < 0) return fail(RAT_ERR_INVALID_ARG, "grid_off[%d] < 0", h);
+    if ((int64_t)grid_cap[h] < max_pos / dilation[h])
+      return fail(RAT_ERR_INVALID_ARG, "grid_cap[%d] = %d < max_pos / D = %lld", h, grid_cap[h],
+                  (long long)(max_pos / dilation[h]));
+    any_grid = any_grid || grid_cap[h] > 0;
+  }
+  if (T == 0) return ok();   // nothing to do; pointers may be NULL
+  const void* ptrs[] = {q, k, v, zk, zv, out, state_k, state_v, ws};
+  const char* names[] = {"q", "k", "v", "zk", "zv", "out", "state_k", "state_v", "ws"};
+  for (int i = 0; i < 9; ++i)
+    if ((st = check_ptr(ptrs[i], names[i], false)) != RAT_OK) return st;
+  if ((st = check_ptr(grid_k, "grid_k", !any_grid)) != RAT_OK) return st;
+  if ((st = check_ptr(grid_v, "grid_v", !any_grid)) != RAT_OK) return st;
+  if ((st = check_ptr(ring_k, "ring_k", W == 0)) != RAT_OK) return st;
+  if ((st = check_ptr(ring_v, "ring_v", W == 0)) != RAT_OK) return st;
+  const ChunkCarve cv = chunk_carve(B, T, H, Dh, dilation, W, p0, dt);
+  if (ws_bytes < cv.total) return fail(RAT_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, cv.total);
+
+  const bool bf16 = dt == RAT_BF16;
+  char* wb = static_cast<char*>(ws);
+  float* h0k = reinterpret_cast<float*>(wb + cv.scan_bytes);
+  float* h0v = h0k + (size_t)B * H * Dh;
+  void* all_k = W > 0 ? wb + cv.scan_bytes + cv.h0_bytes : nullptr;
+  void* all_v = W > 0 ? wb + cv.scan_bytes + cv.h0_bytes + cv.allk_bytes : nullptr;
+  void* vcol = bf16 ? wb + cv.scan_bytes + cv.h0_bytes + cv.allk_bytes + cv.allv_bytes : nullptr;
+
+  rat::HeadTable cache;   // the cache's grid layout
+  std::memset(&cache, 0, sizeof(cache));
+  for (int h = 0; h < H; ++h) {
+    cache.dil[h] = dilation[h];
+    cache.gcap[h] = grid_cap[h];
+    cache.goff[h] = grid_off[h];
+  }
+
+  // 1. the carried states: the scan reads them as h0 and writes h_last over them
+  const size_t sbytes = (size_t)B * H * Dh * sizeof(float);
+  hipError_t e = hipMemcpyAsync(h0k, state_k, sbytes, hipMemcpyDeviceToDevice, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(h0v, state_v, sbytes, hipMemcpyDeviceToDevice, stream);
+  if (e != hipSuccess) return fail(RAT_ERR_HIP, "state copy: %s", hipGetErrorString(e));
+
+  // 2. window states before p0, from the ring
+  if (W > 0 && cv.all_row0 > 0) {
+    rat::RingPrefixPlan rp;
+    rp.ring_k = ring_k; rp.ring_v = ring_v;
+    rp.all_k = all_k; rp.all_v = all_v;
+    rp.B = B; rp.H = H; rp.Dh = Dh; rp.W = W;
+    rp.base = cv.base; rp.n_pre = cv.all_row0;
+    rp.ring_lo = std::max<int64_t>(0, p0 - W + 1);
+    rp.arows = cv.arows; rp.tpad = cv.tpad;
+    rp.bf16 = bf16;
+    e = rat::launch_ring_prefix(rp, stream);
+    if (e != hipSuccess) return fail(RAT_ERR_HIP, "ring prefix launch: %s", hipGetErrorString(e));
+  }
+
+  // 3. the recurrence from the carried states: chunk states, new grid
+  //    entries and ring slots into the cache, final states
+  rat::ScanPlan sp;
+  std::memset(&sp, 0, sizeof(sp));
+  sp.ten[0] = {k, zk, h0k, all_k, grid_k, state_k, rat::kAllToken, rat::kGridHeadRow, W > 0 ? ring_k : nullptr};
+  sp.ten[1] = {v, zv, h0v, all_v, grid_v, state_v, bf16 ? rat::kAllHeadCol : rat::kAllToken, rat::kGridHeadRow,
+               W > 0 ? ring_v : nullptr};
+  sp.ntensors = 2;
+  sp.B = B; sp.T = T; sp.H = H; sp.Dh = Dh;
+  sp.tpad = bf16 ? cv.tpad : cv.arows;
+  sp.p0 = p0;
+  sp.all_row0 = cv.all_row0;
+  sp.arows = cv.arows;
+  sp.W = W;
+  sp.ring_from = std::max<int64_t>(p0, p0 + T - W);
+  sp.bf16 = bf16;
+  sp.heads = cache;
+  sp.ws = ws;
+  sp.fallback_spins = scan_fallback_spins();
+  e = rat::launch_scan(sp, stream);
+  if (e != hipSuccess) return fail(RAT_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
+
+  // 4. bf16: the grid values the chunk's queries see, transposed
+  rat::AttnPlan ap;
+  std::memset(&ap, 0, sizeof(ap));
+  if (bf16) {
+    rat::GridColPlan gp;
+    std::memset(&gp, 0, sizeof(gp));
+    gp.src = grid_v; gp.dst = vcol;
+    gp.B = B; gp.H = H; gp.Dh = Dh;
+    gp.heads = cache;
+    for (int h = 0; h < H; ++h) {
+      gp.vgoff[h] = cv.vgoff[h];
+      gp.vgcap[h] = cv.vgcap[h];
+      gp.rows[h] = cv.rows[h];
+      ap.vgoff[h] = cv.vgoff[h];
+      ap.vgcap[h] = cv.vgcap[h];
+    }
+    e = rat::launch_grid_to_col(gp, stream);
+    if (e != hipSuccess) return fail(RAT_ERR_HIP, "grid transpose launch: %s", hipGetErrorString(e));
+  } else {
+    for (int h = 0; h < H; ++h) {
+      ap.vgoff[h] = grid_off[h];
+      ap.vgcap[h] = grid_cap[h];
+    }
+  }
+
+  // 5. attention of the chunk's queries at absolute positions
+  ap.q = q; ap.out = out;
+  ap.grid_k = grid_k; ap.grid_v = bf16 ? vcol : grid_v;
+  ap.all_k = all_k; ap.all_v = all_v;
+  ap.B = B; ap.T = T; ap.H = H; ap.Dh = Dh; ap.W = W;
+  ap.tpad = bf16 ? cv.tpad : cv.arows;
+  ap.p0 = p0; ap.base = cv.base; ap.arows = cv.arows;
+  ap.bf16 = bf16;
+  ap.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)Dh);
+  ap.heads = cache;
+  e = rat::launch_prefill_attention(ap, stream);
   if (e != hipSuccess) return fail(RAT_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
   return ok();
 }

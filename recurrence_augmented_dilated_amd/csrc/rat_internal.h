@@ -112,13 +112,24 @@ struct ScanTensor {
   float* h_last;       // [B][H][Dh] or null
   int all_mode;        // AllMode of out_all
   int grid_mode;       // GridMode of out_grid
+  void* ring;          // window ring [B][H][W][Dh] (input dtype) or null
 };
 
+// Positions.  Row t of the inputs is absolute position p0 + t: grid entries
+// are the states at absolute positions j with (j + 1) % D == 0 (entry
+// (j + 1) / D - 1), all-state outputs put row t at row (or column)
+// all_row0 + t of a buffer with arows rows, and states at absolute
+// positions >= ring_from also go to ring slot j % W.
 struct ScanPlan {
   ScanTensor ten[2];
   int ntensors;
   int B, T, H, Dh;
-  int64_t tpad;        // row length of kAllHeadCol (multiple of 64, >= T)
+  int64_t tpad;        // row length of kAllHeadCol (multiple of 64, >= all_row0 + T)
+  int64_t p0;          // absolute position of row 0
+  int64_t all_row0;    // all-state row of input row 0 (multiple of 64 for kAllHeadCol)
+  int64_t arows;       // rows of a kAllToken buffer (>= all_row0 + T)
+  int W;               // ring length (ring outputs only)
+  int64_t ring_from;   // first absolute position written to the ring
   int bf16;            // 1: x and outputs are bf16; 0: fp32
   HeadTable heads;
   void* ws;            // workspace base (header + look-back arrays)
@@ -128,20 +139,53 @@ struct ScanPlan {
 size_t scan_workspace_bytes(int ntensors, int B, int T, int H, int Dh);
 hipError_t launch_scan(const ScanPlan& p, hipStream_t s);
 
+// Query row t is absolute position p0 + t; all-state row (or column) r is
+// absolute position base + r (base a multiple of 64).  Grid keys use the
+// head table `heads`; the grid values, `vgoff` / `vgcap` (element offset
+// B * vgoff[h] * Dh, capacity vgcap[h], a multiple of 64 in kGridHeadCol).
 struct AttnPlan {
   const void* q;       // [B][T][H][Dh]
   void* out;           // [B][T][H][Dh]
   const void* grid_k;  // grid states, kGridHeadRow
   const void* grid_v;  // bf16: kGridHeadCol; fp32: kGridHeadRow
-  const void* all_k;   // all states, kAllToken (needed when W > 0)
+  const void* all_k;   // all states, kAllToken with arows rows (needed when W > 0)
   const void* all_v;   // bf16: kAllHeadCol; fp32: kAllToken
   int B, T, H, Dh, W;
   int64_t tpad;
+  int64_t p0, base, arows;
   int bf16;
   float scale;
   HeadTable heads;
+  int64_t vgoff[kMaxHeads];
+  int32_t vgcap[kMaxHeads];
 };
 hipError_t launch_prefill_attention(const AttnPlan& p, hipStream_t s);
+
+// Chunked prefill helpers.
+// Rows [0, n_pre) of the all-state buffers (absolute positions base + r):
+// ring slot (base + r) % W where base + r >= ring_lo, zeros elsewhere.  K in
+// kAllToken with arows rows; V in kAllHeadCol (bf16) or kAllToken (fp32).
+struct RingPrefixPlan {
+  const void* ring_k; const void* ring_v;   // [B][H][W][Dh]
+  void* all_k; void* all_v;
+  int B, H, Dh, W;
+  int64_t base, n_pre, ring_lo, arows, tpad;
+  int bf16;
+};
+hipError_t launch_ring_prefix(const RingPrefixPlan& p, hipStream_t s);
+
+// Grid rows [0, rows[h]) of every (b, h) from the row-major cache layout
+// (heads.goff / heads.gcap) into the column layout (vgoff / vgcap, zero past
+// rows[h] up to vgcap[h]); bf16 only.
+struct GridColPlan {
+  const void* src; void* dst;
+  int B, H, Dh;
+  HeadTable heads;
+  int64_t vgoff[kMaxHeads];
+  int32_t vgcap[kMaxHeads];
+  int32_t rows[kMaxHeads];
+};
+hipError_t launch_grid_to_col(const GridColPlan& p, hipStream_t s);
 
 struct DecodeHeads {
   HeadTable t;                   // dilation, grid capacity and grid offset by head

@@ -104,6 +104,11 @@ struct ScanArgs {
   ScanTensor ten[2];
   int B, T, H, Dh, C;
   int64_t tpad;       // row length of kAllHeadCol outputs
+  int64_t p0;         // absolute position of input row 0
+  int64_t all_row0;   // all-state row of input row 0
+  int64_t arows;      // rows of kAllToken outputs
+  int W;              // ring length
+  int64_t ring_from;  // first absolute position stored in the ring
   int n_slabs;        // ntensors * B * slabs_per_bt
   int slabs_per_bt;   // C / (64 * NC)
   uint64_t* agg_a;
@@ -324,9 +329,10 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
   for (int c = 0; c < NC; ++c) hv[c] = s_carry[wave][lane * NC + c];
 
   const int D = tn.grid_mode == kGridToken ? a.heads.dil[0] : a.heads.dil[h];
-  // first grid position >= t0: smallest j >= t0 with (j + 1) % D == 0
-  int next_grid = (t0 / D) * D + (D - 1);
-  if (next_grid < t0) next_grid += D;
+  // first grid position >= p0 + t0 (absolute): smallest j with (j + 1) % D == 0
+  const int64_t ja0 = a.p0 + t0;
+  int64_t next_grid = (ja0 / D) * D + (D - 1);
+  if (next_grid < ja0) next_grid += D;
   XT* out_all = static_cast<XT*>(tn.out_all);
   XT* out_grid = static_cast<XT*>(tn.out_grid);
   const int64_t G_tok = T / D;
@@ -349,9 +355,9 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
         gate_pair(Z::get(zr[s], c), g, cc);
         hv[c] = g * hv[c] + cc * V::get(xr[s], c);
       }
-      if (tok_all) V::store(out_all + ((int64_t)b * T + t) * C + cs * SC + lo, hv);
-      if (out_grid && t == next_grid) {
-        const int64_t i = (t + 1) / D - 1;
+      if (tok_all) V::store(out_all + ((int64_t)b * a.arows + a.all_row0 + t) * C + cs * SC + lo, hv);
+      if (out_grid && a.p0 + t == next_grid) {
+        const int64_t i = (a.p0 + t + 1) / D - 1;
         if (tn.grid_mode == kGridToken) {
           V::store(out_grid + (((int64_t)b * G_tok + i) * a.H + h) * a.Dh + d, hv);
         } else if (tn.grid_mode == kGridHeadRow) {
@@ -367,6 +373,10 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) tn.h_last[((int64_t)b * a.H + h) * a.Dh + d + c] = hv[c];
       }
+      if (tn.ring && a.p0 + t >= a.ring_from) {
+        const int64_t slot = (a.p0 + t) % a.W;
+        V::store(static_cast<XT*>(tn.ring) + (((int64_t)b * a.H + h) * a.W + slot) * a.Dh + d, hv);
+      }
     }
     if (col_all) {
       // keys t-3..t of each channel; positions past T are written as zeros
@@ -378,10 +388,10 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
 #pragma unroll
           for (int c = 0; c < NC; ++c)
             store4(reinterpret_cast<bf16_t*>(s_T + (lane * NC + c) * kTRow) + wave * kLW + (s - 3), run[c]);
-        } else if (t - 3 < a.tpad) {
+        } else if (a.all_row0 + t - 3 < a.tpad) {
 #pragma unroll
           for (int c = 0; c < NC; ++c)
-            store4(out_all + col_all_row + (int64_t)c * a.tpad + col_key_pos(t - 3, d + c), run[c]);
+            store4(out_all + col_all_row + (int64_t)c * a.tpad + col_key_pos(a.all_row0 + t - 3, d + c), run[c]);
         }
       }
     }
@@ -393,7 +403,7 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
       // of a 64-key tile holds logical chunk c = p ^ col_swz(d): keys
       // 16(c/2) + 4(c%2) + {0..3} and the four keys 8 further on.
       __syncthreads();
-      const int64_t key0 = (int64_t)chunk * kChunkT;
+      const int64_t key0 = a.all_row0 + (int64_t)chunk * kChunkT;   // a multiple of 64
       constexpr int CPR = kChunkT / 8;   // 16-byte chunks per channel row
 #pragma unroll
       for (int k = 0; k < SC * CPR / (kNW * 64); ++k) {
@@ -417,7 +427,7 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
   // the wave holding position T-1 zero-fills the column grid past its last entry
   if (col_grid && t0 <= T - 1 && T - 1 < t0 + kLW) {
     const int cap = a.heads.gcap[h];
-    for (int i = T / D; i < cap; ++i) {
+    for (int64_t i = (a.p0 + T) / D; i < cap; ++i) {
 #pragma unroll
       for (int c = 0; c < NC; ++c)
         store1(out_grid + col_grid_row + (int64_t)c * cap + col_key_pos(i, d + c), 0.f);
@@ -456,6 +466,11 @@ hipError_t launch_scan(const ScanPlan& p, hipStream_t s) {
   a.ten[1] = p.ntensors > 1 ? p.ten[1] : p.ten[0];
   a.B = p.B; a.T = p.T; a.H = p.H; a.Dh = p.Dh; a.C = p.H * p.Dh;
   a.tpad = p.tpad;
+  a.p0 = p.p0;
+  a.all_row0 = p.all_row0;
+  a.arows = p.arows > 0 ? p.arows : p.T;
+  a.W = p.W;
+  a.ring_from = p.ring_from;
   a.heads = p.heads;
   a.fallback_spins = p.fallback_spins >= 0 ? uint32_t(p.fallback_spins) : kFallbackSpins;
   const int nc = pick_nc(a.C);

@@ -109,3 +109,37 @@ def test_grid_layout():
     assert cap == [132096, 8256, 2064]
     assert off == [0, 132096, 132096 + 8256]
     assert rows == sum(cap)
+
+
+def test_prefill_chunk_validation():
+    L = R.lib()
+    H = 2
+    d = (ctypes.c_int32 * H)(4, 16)
+    off = (ctypes.c_int64 * H)(0, 64)
+    cap_ok = (ctypes.c_int32 * H)(64, 16)
+    cap_bad = (ctypes.c_int32 * H)(63, 16)
+
+    def call(p0=64, T=128, max_pos=256, cap=cap_ok, W=8, ring=FAKE, wsb=0, q=FAKE, dil=d):
+        return L.rat_prefill_chunk(q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, off, cap, ring,
+                                   ring, p0, max_pos, 1, T, H, 128, dil, W, -1.0, 1, FAKE, wsb, None)
+
+    assert call(p0=32) == -2                 # chunk start must be a multiple of 64
+    assert call(p0=-64) == -1
+    assert call(T=193) == -1                 # p0 + T > max_pos
+    assert call(max_pos=1 << 31) == -1       # positions must fit in 31 bits
+    assert call(cap=cap_bad) == -1           # grid capacity below max_pos / D
+    assert call(ring=None) == -1             # W > 0 needs ring buffers
+    assert call(q=None) == -1
+    assert call(q=MIS) == -1
+    assert call(dil=None) == -1
+    assert call(W=-1) == -1
+    assert call() == -3                      # workspace too small
+    assert call(T=0, q=None, ring=None) == 0  # empty chunk: no-op, NULL buffers allowed
+
+
+def test_prefill_chunk_workspace_size():
+    a = R.rat_prefill_chunk_workspace_size(1, 1024, 16, 128, 16, 0, 0)
+    b = R.rat_prefill_chunk_workspace_size(1, 1024, 16, 128, 16, 128, 0)
+    c = R.rat_prefill_chunk_workspace_size(1, 1024, 16, 128, 16, 128, 4096)
+    assert 0 < a < b < c          # window buffers; later chunks also hold the ring prefix and more grid
+    assert R.rat_prefill_chunk_workspace_size(1, 1024, 16, 128, 16, 0, -64) == 0
