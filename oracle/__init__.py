@@ -6,3 +6,4 @@ import this package.  The product path never does.
 from .rat_oracle import (  # noqa: F401
     DecodeCache, attend, default_scale, gates, key_set, pairs, prefill, scan,
 )
+from . import topk_oracle  # noqa: F401,E402

@@ -356,3 +356,191 @@ def run_all(O):
             failed.append(pin.__name__)
     return failed
 
+
+
+# ---------------------------------------------------------------------------
+# top-k block attention over the memory states (oracle.topk_oracle)
+# ---------------------------------------------------------------------------
+
+def tpin_golden(T):
+    f = _golden("topk_hand.json")
+    K = np.asarray(f["keys"], dtype=np.float64)
+    blk, t, q = f["block"], f["t"], np.asarray(f["q"])
+    kmin, kmax, kmean = T.block_stats(K.reshape(1, -1, 1, 2), blk)
+    for meth, name in ((T.QUEST, "quest"), (T.MOBA, "moba")):
+        for j, want in f[f"{name}_scores"].items():
+            j = int(j)
+            got = T.block_score(q, kmin[0, j, 0], kmax[0, j, 0], kmean[0, j, 0], meth)
+            _close(got, want, 1e-15, f"{name} score of block {j}")
+        scores = [T.block_score(q, kmin[0, j, 0], kmax[0, j, 0], kmean[0, j, 0], meth) for j in range(t // blk)]
+        chosen = T.select_blocks(t, blk, f["topk"], scores)
+        assert chosen == f[f"{name}_chosen"], (name, chosen)
+        assert list(T.key_positions(t, blk, chosen)) == f[f"{name}_positions"], name
+
+
+def tpin_quest_is_box_maximum(T):
+    """Quest's score is the maximum of q.k over the corners of the block's
+    bounding box (brute force over the 2^Dh corners), hence an upper bound of
+    q.k for every key in the block."""
+    rng = _rng(21)
+    Dh, blk = 4, 5
+    K = rng.normal(size=(1, 3 * blk, 1, Dh))
+    kmin, kmax, kmean = T.block_stats(K, blk)
+    for trial in range(20):
+        q = rng.normal(size=Dh)
+        for j in range(3):
+            s = T.block_score(q, kmin[0, j, 0], kmax[0, j, 0], kmean[0, j, 0], T.QUEST)
+            corners = [np.where([(c >> d) & 1 for d in range(Dh)], kmax[0, j, 0], kmin[0, j, 0]) for c in range(2 ** Dh)]
+            _close(s, max(float(q @ c) for c in corners), 1e-12, "quest == max over box corners")
+            rows = K[0, j * blk:(j + 1) * blk, 0]
+            assert s >= np.max(rows @ q) - 1e-12, "quest is an upper bound"
+
+
+def tpin_moba_is_mean_dot(T):
+    """MoBA's score is the average of the block's per-key dot products."""
+    rng = _rng(22)
+    Dh, blk = 6, 4
+    K = rng.normal(size=(2, 3 * blk + 1, 1, Dh))
+    kmin, kmax, kmean = T.block_stats(K, blk)
+    assert kmean.shape[1] == 3                 # the incomplete last block has no representative
+    for b in range(2):
+        for j in range(3):
+            q = rng.normal(size=Dh)
+            dots = [float(q @ K[b, p, 0]) for p in range(j * blk, (j + 1) * blk)]
+            s = T.block_score(q, kmin[b, j, 0], kmax[b, j, 0], kmean[b, j, 0], T.MOBA)
+            _close(s, sum(dots) / blk, 1e-12, "moba == mean of per-key dots")
+            _close(kmin[b, j, 0], [min(K[b, p, 0, d] for p in range(j * blk, (j + 1) * blk)) for d in range(Dh)],
+                   0.0, "block minimum")
+            _close(kmax[b, j, 0], [max(K[b, p, 0, d] for p in range(j * blk, (j + 1) * blk)) for d in range(Dh)],
+                   0.0, "block maximum")
+
+
+def tpin_selection_bruteforce(T):
+    """The chosen blocks are the subset of candidates with the largest score
+    sum (enumerating every subset of size topk); among equal sums, the one
+    with the lower block indices."""
+    import itertools
+    rng = _rng(23)
+    blk = 4
+    for trial in range(60):
+        local = int(rng.integers(1, 9))
+        t = local * blk + int(rng.integers(0, blk))
+        topk = int(rng.integers(0, 6))
+        scores = np.round(rng.normal(size=local), 1) if trial % 3 else rng.normal(size=local)   # ties sometimes
+        cand = list(range(1, local))
+        if len(cand) <= topk:
+            want = cand
+        else:
+            best = None
+            for sub in itertools.combinations(cand, topk):
+                key = (-sum(scores[j] for j in sub), sorted(sub))
+                if best is None or key < best:
+                    best = key
+            want = list(best[1])
+            # the tie rule: equal-sum subsets resolved towards lower indices only matter when
+            # scores tie; the top-k set then prefers lower indices element by element
+            ranked = sorted(cand, key=lambda j: (-scores[j], j))[:topk]
+            assert sorted(ranked) == want or sum(scores[j] for j in ranked) == -best[0]
+        got = T.select_blocks(t, blk, topk, scores)
+        assert got == sorted(got)
+        if len(cand) > topk:
+            _close(sum(scores[j] for j in got), sum(scores[j] for j in want), 1e-12, "top-k score sum")
+            # ties: every chosen block scores >= every unchosen candidate, and a
+            # tie between a chosen and an unchosen block goes to the lower index
+            for u in set(cand) - set(got):
+                for c in got:
+                    assert scores[c] > scores[u] or (scores[c] == scores[u] and c < u), (got, u, scores)
+        else:
+            assert got == want
+
+
+def tpin_ties_prefer_lower_blocks(T):
+    """Equal scores: the lowest-indexed candidates are chosen."""
+    for local in range(2, 12):
+        for topk in range(0, local):
+            t = local * 8 + 3
+            got = T.select_blocks(t, 8, topk, np.zeros(local))
+            assert got == list(range(1, min(local, topk + 1))), (local, topk, got)
+
+
+def tpin_prefill_selects_by_key_states(T):
+    """The selections made inside topk_prefill are the top-k of scores
+    recomputed here from the key states (per-key dot products for MoBA,
+    per-key corner maxima for Quest)."""
+    import oracle.rat_oracle as O
+    rng = _rng(26)
+    B, L, H, Dh, blk, topk = 1, 48, 2, 4, 4, 3
+    q, k, v = (rng.normal(size=(B, L, H, Dh)) for _ in range(3))
+    zk, zv = rng.normal(0.5, 1, size=(2, B, L, H, Dh))
+    Kt = O.scan(k, zk)
+    for meth in (T.QUEST, T.MOBA):
+        _, chosen = T.topk_prefill(q, k, v, zk, zv, blk, topk, meth)
+        for (b, t, h), sel in chosen.items():
+            local = t // blk
+            scores = np.full(max(local, 1), -np.inf)
+            for j in range(1, local):
+                rows = Kt[b, j * blk:(j + 1) * blk, h]
+                if meth == T.MOBA:
+                    scores[j] = np.mean(rows @ q[b, t, h])
+                else:
+                    scores[j] = np.sum(np.max(rows * q[b, t, h], axis=0))
+            cand = list(range(1, local))
+            want = cand if len(cand) <= topk else sorted(sorted(cand, key=lambda j: (-scores[j], j))[:topk])
+            assert sel == want, (meth, b, t, h, sel, want)
+
+
+def tpin_key_positions_bruteforce(T):
+    blk = 3
+    for t in range(0, 40):
+        local = t // blk
+        for chosen in ([], [1], [2, 5], list(range(1, local))):
+            chosen = [j for j in chosen if 1 <= j < local]
+            want = [p for p in range(t + 1) if (p // blk) in ({0, local} | set(chosen))]
+            assert list(T.key_positions(t, blk, chosen)) == want, (t, chosen)
+
+
+def tpin_all_blocks_is_dense(T):
+    """With topk at least the number of candidate blocks every position
+    0..t is a key: causal attention over the states (rat_oracle with D = 1)."""
+    import oracle.rat_oracle as O
+    rng = _rng(24)
+    B, L, H, Dh = 1, 40, 2, 8
+    q, k, v = (rng.normal(size=(B, L, H, Dh)) for _ in range(3))
+    zk, zv = rng.normal(1, 1, size=(2, B, L, H, Dh))
+    for meth in (T.QUEST, T.MOBA):
+        out, _ = T.topk_prefill(q, k, v, zk, zv, 4, 100, meth)
+        _close(out, O.prefill(q, k, v, zk, zv, 1, 0), 1e-12, f"{meth} with every block == dense")
+
+
+def tpin_first_and_local_only(T):
+    """topk = 0 keeps the first and the local block: attention over those
+    positions by a dense masked softmax (a [T, T] score matrix)."""
+    import oracle.rat_oracle as O
+    rng = _rng(25)
+    B, L, H, Dh, blk = 1, 37, 1, 4, 5
+    q, k, v = (rng.normal(size=(B, L, H, Dh)) for _ in range(3))
+    zk, zv = rng.normal(1, 1, size=(2, B, L, H, Dh))
+    Kt, Vt = O.scan(k, zk), O.scan(v, zv)
+    mask = np.zeros((L, L), dtype=bool)
+    for t in range(L):
+        for p in range(t + 1):
+            mask[t, p] = p < blk or p // blk == t // blk
+    want = _masked_softmax_attention(q[0, :, 0], Kt[0, :, 0], Vt[0, :, 0], mask, 1.0 / math.sqrt(Dh))
+    out, _ = T.topk_prefill(q, k, v, zk, zv, blk, 0, T.QUEST)
+    out = out[0, :, 0]
+    _close(out, want, 1e-12, "first + local blocks")
+
+
+TOPK_PINS = [tpin_golden, tpin_quest_is_box_maximum, tpin_moba_is_mean_dot, tpin_selection_bruteforce,
+             tpin_ties_prefer_lower_blocks, tpin_prefill_selects_by_key_states, tpin_key_positions_bruteforce,
+             tpin_all_blocks_is_dense, tpin_first_and_local_only]
+
+
+def run_topk(T):
+    failed = []
+    for p in TOPK_PINS:
+        try:
+            p(T)
+        except Exception as e:  # noqa: BLE001
+            failed.append(f"{p.__name__}: {type(e).__name__}: {e}")
+    return failed

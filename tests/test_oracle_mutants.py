@@ -75,3 +75,54 @@ def test_mutant_is_caught(name):
     old, new = MUTANTS[name]
     failed = oracle_pins.run_all(_mutant(old, new))
     assert failed, f"no pin catches the mutant: {name}"
+
+
+# top-k block attention oracle (oracle/topk_oracle.py) against its own pins
+import oracle.topk_oracle as real_topk  # noqa: E402
+
+TOPK_MUTANTS = {
+    "quest keeps only the minimum corner": (
+        "np.maximum(q * kmin, q * kmax)", "q * kmin"),
+    "quest takes the lower corner": (
+        "np.maximum(q * kmin, q * kmax)", "np.minimum(q * kmin, q * kmax)"),
+    "moba pools a sum instead of a mean": (
+        "kmean[:, j] = rows.sum(axis=1) / block", "kmean[:, j] = rows.sum(axis=1)"),
+    "block statistics drop the last position": (
+        "rows = Kt[:, j * block:(j + 1) * block]", "rows = Kt[:, j * block:(j + 1) * block - 1]"),
+    "selection keeps the lowest scores": (
+        "key=lambda j: (-scores[j], j)", "key=lambda j: (scores[j], j)"),
+    "ties go to the higher block": (
+        "key=lambda j: (-scores[j], j)", "key=lambda j: (-scores[j], -j)"),
+    "first block is a candidate": (
+        "cand = list(range(1, local))", "cand = list(range(0, local))"),
+    "local block is a candidate": (
+        "cand = list(range(1, local))", "cand = list(range(1, local + 1))"),
+    "first block not kept": (
+        "blocks = sorted(set([0, local]) | set(chosen))", "blocks = sorted(set([local]) | set(chosen))"),
+    "local block not kept": (
+        "blocks = sorted(set([0, local]) | set(chosen))", "blocks = sorted(set([0]) | set(chosen))"),
+    "local block runs past the query": (
+        "hi = min((j + 1) * block - 1, t)", "hi = (j + 1) * block - 1"),
+    "scores computed from the values": (
+        "kmin, kmax, kmean = block_stats(Kt, block)\n    out", "kmin, kmax, kmean = block_stats(Vt, block)\n    out"),
+}
+
+
+def _topk_mutant(old, new):
+    src = inspect.getsource(real_topk)
+    assert src.count(old) >= 1, f"mutation site not found: {old!r}"
+    src = src.replace(old, new).replace("from .rat_oracle import", "from oracle.rat_oracle import")
+    mod = types.ModuleType("topk_mutant")
+    exec(compile(src, "topk_mutant", "exec"), mod.__dict__)  # noqa: S102
+    return mod
+
+
+def test_real_topk_oracle_passes_every_pin():
+    assert oracle_pins.run_topk(real_topk) == []
+
+
+@pytest.mark.parametrize("name", list(TOPK_MUTANTS))
+def test_topk_mutant_is_caught(name):
+    old, new = TOPK_MUTANTS[name]
+    failed = oracle_pins.run_topk(_topk_mutant(old, new))
+    assert failed, f"no pin catches the mutant: {name}"

@@ -8,3 +8,8 @@ from tests import oracle_pins
 @pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda p: p.__name__)
 def test_pin(pin):
     pin(oracle.rat_oracle)
+
+
+@pytest.mark.parametrize("pin", oracle_pins.TOPK_PINS, ids=lambda p: p.__name__)
+def test_topk_pin(pin):
+    pin(oracle.topk_oracle)
