@@ -231,6 +231,62 @@ rat_status_t rat_decode_step(const void* q, const void* k, const void* v, const 
                              const int32_t* dilation, int32_t W, float scale, rat_dtype_t dtype,
                              void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------ *
+ * Top-k block attention over the memory states ("Augmenting Attention with
+ * Exponentially Decaying Memory Improves Query-Aware KV Sparsity", sections
+ * 2.2 and 3; RAT+ Fig. 3 and Tables 17-18).  Positions are cut into blocks of
+ * `block` positions.  A query at position t attends over the recurrent
+ * states of the first block, of its own block (up to t) and of the `topk`
+ * complete blocks between them with the highest scores (all of them when
+ * there are at most topk; ties go to the lower block index):
+ *   RAT_TOPK_QUEST  score = sum_d max(q_d * min_d, q_d * max_d) over the
+ *                   dimension-wise min / max of the block's key states;
+ *   RAT_TOPK_MOBA   score = q . mean of the block's key states.
+ *
+ * Caches (device, caller-owned):
+ *   cache_k/_v  every recurrent state, dtype, [H][B][max_pos][Dh] (the grid
+ *               layout of rat_grid_layout with dilation 1 on every head)
+ *   summary     fp32 [H][B][max_pos / block][3][Dh]: min, max and mean of
+ *               the key states of each complete block
+ *   state_k/_v  fp32 [B][H][Dh]: the state after the last cached position
+ *               (zeros before the first call)
+ * Limits: 1 <= block <= 1024, 0 <= topk <= 128, max_pos / block <= 8192,
+ * max_pos < 2^31.
+ *
+ * chosen (device int32, optional): per query the selected blocks in
+ * ascending order, -1 in unused slots.
+ * ------------------------------------------------------------------------ */
+typedef enum { RAT_TOPK_QUEST = 0, RAT_TOPK_MOBA = 1 } rat_topk_score_t;
+
+/* Prefill positions p0 .. p0+T-1 (any p0 >= 0, p0 + T <= max_pos) of
+ * sequences whose positions before p0 are cached: recurrence from state_k/_v,
+ * every new state into the caches, summaries of the blocks completed, then
+ * top-k block attention for every row.  q, k, v, zk, zv, out as
+ * rat_dilated_prefill; chosen [B][T][H][topk] or NULL. */
+size_t rat_topk_prefill_workspace_size(int32_t B, int32_t T, int32_t H, int32_t Dh);
+rat_status_t rat_topk_prefill(const void* q, const void* k, const void* v, const float* zk,
+                              const float* zv, void* out, int32_t* chosen, float* state_k,
+                              float* state_v, void* cache_k, void* cache_v, float* summary,
+                              int64_t p0, int64_t max_pos, int32_t B, int32_t T, int32_t H,
+                              int32_t Dh, int32_t block, int32_t topk, rat_topk_score_t score,
+                              float scale, rat_dtype_t dtype, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+/* One new token per sequence at position pos[b] (device int32 [B], every
+ * entry in [0, max_pos), others: error bit 1 and a zero output): state
+ * update, cache row pos[b], the summary of a block that row completes, then
+ * top-k block attention of q.  q, k, v [B][H][Dh] dtype; zk, zv fp32; out
+ * [B][H][Dh]; chosen [B][H][topk] or NULL; ws of at least
+ * rat_topk_decode_workspace_size() bytes (its header carries the error word). */
+size_t rat_topk_decode_workspace_size(void);
+rat_status_t rat_topk_decode_step(const void* q, const void* k, const void* v, const float* zk,
+                                  const float* zv, float* state_k, float* state_v, void* cache_k,
+                                  void* cache_v, float* summary, const int32_t* pos,
+                                  int64_t max_pos, void* out, int32_t* chosen, int32_t B, int32_t H,
+                                  int32_t Dh, int32_t block, int32_t topk, rat_topk_score_t score,
+                                  float scale, rat_dtype_t dtype, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

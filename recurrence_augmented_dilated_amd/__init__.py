@@ -83,6 +83,16 @@ def lib():
             L.rat_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, c_i64,
                                             c_i64, c_int, c_int, c_int, c_int, vp, c_int, c_f, c_int, vp,
                                             c_sz, vp]
+            L.rat_topk_prefill_workspace_size.restype = c_sz
+            L.rat_topk_prefill_workspace_size.argtypes = [c_int, c_int, c_int, c_int]
+            L.rat_topk_prefill.restype = c_int
+            L.rat_topk_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, c_i64, c_i64, c_int,
+                                           c_int, c_int, c_int, c_int, c_int, c_int, c_f, c_int, vp, c_sz, vp]
+            L.rat_topk_decode_workspace_size.restype = c_sz
+            L.rat_topk_decode_workspace_size.argtypes = []
+            L.rat_topk_decode_step.restype = c_int
+            L.rat_topk_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, c_i64, vp, vp, c_int,
+                                               c_int, c_int, c_int, c_int, c_int, c_f, c_int, vp, c_sz, vp]
             _lib = L
     return _lib
 
@@ -289,6 +299,63 @@ def rat_prefill_chunk(q, k, v, zk, zv, state_k, state_v, grid_k, grid_v, grid_of
         _ptr(q), _ptr(k), _ptr(v), _ptr(zk), _ptr(zv), _ptr(out), _ptr(state_k), _ptr(state_v),
         _ptr(grid_k), _ptr(grid_v), off, cap, _ptr(ring_k), _ptr(ring_v), int(p0), int(max_pos), B, T, H,
         Dh, _i32_array(dil), int(W), s, _dtype_code(q), _ptr(ws), ws.numel(), _stream(q.device)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# top-k block attention over the memory states
+# ---------------------------------------------------------------------------
+
+TOPK_QUEST, TOPK_MOBA = 0, 1
+
+
+def topk_cache(B, H, Dh, max_pos, block, dtype=torch.bfloat16, device="cuda:0"):
+    """Zeroed state caches for top-k block attention: dict(state_k, state_v
+    fp32 [B, H, Dh]; cache_k, cache_v [H, B, max_pos, Dh]; summary fp32
+    [H, B, max_pos // block, 3, Dh])."""
+    return dict(state_k=torch.zeros((B, H, Dh), dtype=torch.float32, device=device),
+                state_v=torch.zeros((B, H, Dh), dtype=torch.float32, device=device),
+                cache_k=torch.zeros((H, B, max_pos, Dh), dtype=dtype, device=device),
+                cache_v=torch.zeros((H, B, max_pos, Dh), dtype=dtype, device=device),
+                summary=torch.zeros((H, B, max_pos // block, 3, Dh), dtype=torch.float32, device=device))
+
+
+def rat_topk_prefill(q, k, v, zk, zv, cache, p0, max_pos, block, topk, score=TOPK_QUEST, scale=None,
+                     out=None, chosen=None, ws=None):
+    """Top-k block attention prefill of positions p0 .. p0+T-1 (extends the
+    caches in `cache`, see topk_cache); returns out [B, T, H, Dh] (and fills
+    `chosen` [B, T, H, topk] int32 if given)."""
+    B, T, H, Dh = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if ws is None:
+        ws = workspace(int(lib().rat_topk_prefill_workspace_size(B, T, H, Dh)), q.device, "topk_prefill")
+    s = -1.0 if scale is None else float(scale)
+    _check(lib().rat_topk_prefill(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(zk), _ptr(zv), _ptr(out), _ptr(chosen), _ptr(cache["state_k"]),
+        _ptr(cache["state_v"]), _ptr(cache["cache_k"]), _ptr(cache["cache_v"]), _ptr(cache["summary"]), int(p0),
+        int(max_pos), B, T, H, Dh, int(block), int(topk), int(score), s, _dtype_code(q), _ptr(ws), ws.numel(),
+        _stream(q.device)))
+    return out
+
+
+def rat_topk_decode_step(q, k, v, zk, zv, cache, pos, max_pos, block, topk, score=TOPK_QUEST, scale=None,
+                         out=None, chosen=None, ws=None):
+    """One top-k block attention decode step at positions pos (int32 [B]);
+    returns out [B, H, Dh] (and fills `chosen` [B, H, topk] if given)."""
+    B, H, Dh = q.shape
+    if pos.dtype != torch.int32:
+        raise TypeError("pos must be int32")
+    if out is None:
+        out = torch.empty_like(q)
+    if ws is None:
+        ws = workspace(int(lib().rat_topk_decode_workspace_size()), q.device, "topk_decode")
+    s = -1.0 if scale is None else float(scale)
+    _check(lib().rat_topk_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(zk), _ptr(zv), _ptr(cache["state_k"]), _ptr(cache["state_v"]),
+        _ptr(cache["cache_k"]), _ptr(cache["cache_v"]), _ptr(cache["summary"]), _ptr(pos), int(max_pos), _ptr(out),
+        _ptr(chosen), B, H, Dh, int(block), int(topk), int(score), s, _dtype_code(q), _ptr(ws), ws.numel(),
+        _stream(q.device)))
     return out
 
 

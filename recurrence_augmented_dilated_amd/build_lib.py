@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librat.so")
-SOURCES = ["scan.hip", "prefill_attn.hip", "decode.hip", "chunk.hip", "rat_api.cpp"]
+SOURCES = ["scan.hip", "prefill_attn.hip", "decode.hip", "chunk.hip", "topk.hip", "rat_api.cpp"]
 
 ARCH = "gfx950"
 FLAGS = [

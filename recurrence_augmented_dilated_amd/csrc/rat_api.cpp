@@ -563,3 +563,161 @@ rat_status_t rat_decode_step(const void* q, const void* k, const void* v, const 
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// top-k block attention
+// ---------------------------------------------------------------------------
+namespace {
+
+rat_status_t check_topk(int32_t block, int32_t topk, rat_topk_score_t score, int64_t max_pos) {
+  if (block < 1 || block > 1024) return fail(RAT_ERR_INVALID_ARG, "block must be in [1, 1024] (got %d)", block);
+  if (topk < 0 || topk > rat::kTopkMaxK)
+    return fail(RAT_ERR_INVALID_ARG, "topk must be in [0, %d] (got %d)", rat::kTopkMaxK, topk);
+  if (score != RAT_TOPK_QUEST && score != RAT_TOPK_MOBA)
+    return fail(RAT_ERR_INVALID_ARG, "unknown block score %d", (int)score);
+  if (max_pos < 1 || max_pos > INT32_MAX)
+    return fail(RAT_ERR_INVALID_ARG, "max_pos must be in [1, 2^31) (got %lld)", (long long)max_pos);
+  if (max_pos / block > rat::kTopkMaxBlocks)
+    return fail(RAT_ERR_UNSUPPORTED, "max_pos / block = %lld exceeds %d blocks", (long long)(max_pos / block),
+                rat::kTopkMaxBlocks);
+  return RAT_OK;
+}
+
+// the scan writes every state into the [H][B][max_pos][Dh] caches: the grid
+// layout with dilation 1 and capacity max_pos on every head
+void dense_cache_table(int32_t H, int64_t max_pos, rat::HeadTable& ht) {
+  std::memset(&ht, 0, sizeof(ht));
+  for (int h = 0; h < H; ++h) {
+    ht.dil[h] = 1;
+    ht.gcap[h] = (int32_t)max_pos;
+    ht.goff[h] = (int64_t)h * max_pos;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t rat_topk_prefill_workspace_size(int32_t B, int32_t T, int32_t H, int32_t Dh) {
+  if (check_common(B, T, H, Dh, RAT_BF16) != RAT_OK) return 0;
+  return align_up(rat::scan_workspace_bytes(2, B, T, H, Dh)) + align_up((size_t)2 * B * H * Dh * sizeof(float));
+}
+
+rat_status_t rat_topk_prefill(const void* q, const void* k, const void* v, const float* zk,
+                              const float* zv, void* out, int32_t* chosen, float* state_k,
+                              float* state_v, void* cache_k, void* cache_v, float* summary,
+                              int64_t p0, int64_t max_pos, int32_t B, int32_t T, int32_t H,
+                              int32_t Dh, int32_t block, int32_t topk, rat_topk_score_t score,
+                              float scale, rat_dtype_t dt, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  rat_status_t st = check_common(B, T, H, Dh, dt);
+  if (st != RAT_OK) return st;
+  if ((st = check_topk(block, topk, score, max_pos)) != RAT_OK) return st;
+  if (p0 < 0) return fail(RAT_ERR_INVALID_ARG, "p0 must be >= 0 (got %lld)", (long long)p0);
+  if (p0 + T > max_pos)
+    return fail(RAT_ERR_INVALID_ARG, "p0 + T = %lld exceeds max_pos = %lld", (long long)(p0 + T),
+                (long long)max_pos);
+  if (T == 0) return ok();
+  const void* ptrs[] = {q, k, v, zk, zv, out, state_k, state_v, cache_k, cache_v, summary, ws};
+  const char* names[] = {"q", "k", "v", "zk", "zv", "out", "state_k", "state_v", "cache_k", "cache_v",
+                         "summary", "ws"};
+  for (int i = 0; i < 12; ++i)
+    if ((st = check_ptr(ptrs[i], names[i], false)) != RAT_OK) return st;
+  if ((st = check_ptr(chosen, "chosen", true)) != RAT_OK) return st;
+  const size_t need = rat_topk_prefill_workspace_size(B, T, H, Dh);
+  if (ws_bytes < need) return fail(RAT_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+
+  const bool bf16 = dt == RAT_BF16;
+  const size_t scan_bytes = align_up(rat::scan_workspace_bytes(2, B, T, H, Dh));
+  float* h0k = reinterpret_cast<float*>(static_cast<char*>(ws) + scan_bytes);
+  float* h0v = h0k + (size_t)B * H * Dh;
+  const size_t sbytes = (size_t)B * H * Dh * sizeof(float);
+  hipError_t e = hipMemcpyAsync(h0k, state_k, sbytes, hipMemcpyDeviceToDevice, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(h0v, state_v, sbytes, hipMemcpyDeviceToDevice, stream);
+  if (e != hipSuccess) return fail(RAT_ERR_HIP, "state copy: %s", hipGetErrorString(e));
+
+  // recurrence: every state of positions p0 .. p0+T-1 into the caches
+  rat::ScanPlan sp;
+  std::memset(&sp, 0, sizeof(sp));
+  sp.ten[0] = {k, zk, h0k, nullptr, cache_k, state_k, rat::kAllToken, rat::kGridHeadRow, nullptr};
+  sp.ten[1] = {v, zv, h0v, nullptr, cache_v, state_v, rat::kAllToken, rat::kGridHeadRow, nullptr};
+  sp.ntensors = 2;
+  sp.B = B; sp.T = T; sp.H = H; sp.Dh = Dh;
+  sp.tpad = T;
+  sp.p0 = p0;
+  sp.arows = T;
+  sp.bf16 = bf16;
+  dense_cache_table(H, max_pos, sp.heads);
+  sp.ws = ws;
+  sp.fallback_spins = scan_fallback_spins();
+  e = rat::launch_scan(sp, stream);
+  if (e != hipSuccess) return fail(RAT_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
+
+  rat::TopkPlan tp;
+  std::memset(&tp, 0, sizeof(tp));
+  tp.q = q; tp.out = out; tp.chosen = chosen;
+  tp.cache_k = cache_k; tp.cache_v = cache_v; tp.summary = summary;
+  tp.p0 = p0; tp.max_pos = max_pos;
+  tp.B = B; tp.T = T; tp.H = H; tp.Dh = Dh; tp.block = block; tp.topk = topk; tp.score = (int)score;
+  tp.bf16 = bf16;
+  tp.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)Dh);
+  // summaries of the blocks whose last position falls in this call
+  const int64_t j_lo = (p0 + block) / block - 1;        // first j with (j + 1) * block - 1 >= p0
+  const int64_t j_hi = (p0 + T) / block;                 // j with (j + 1) * block <= p0 + T
+  e = rat::launch_topk_stats(tp, j_lo, j_hi, stream);
+  if (e != hipSuccess) return fail(RAT_ERR_HIP, "block summary launch: %s", hipGetErrorString(e));
+  e = rat::launch_topk_attend(tp, stream);
+  if (e != hipSuccess) return fail(RAT_ERR_HIP, "top-k attention launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t rat_topk_decode_workspace_size(void) { return sizeof(rat::WsHeader); }
+
+rat_status_t rat_topk_decode_step(const void* q, const void* k, const void* v, const float* zk,
+                                  const float* zv, float* state_k, float* state_v, void* cache_k,
+                                  void* cache_v, float* summary, const int32_t* pos,
+                                  int64_t max_pos, void* out, int32_t* chosen, int32_t B, int32_t H,
+                                  int32_t Dh, int32_t block, int32_t topk, rat_topk_score_t score,
+                                  float scale, rat_dtype_t dt, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  rat_status_t st = check_common(B, 0, H, Dh, dt);
+  if (st != RAT_OK) return st;
+  if ((st = check_topk(block, topk, score, max_pos)) != RAT_OK) return st;
+  const void* ptrs[] = {q, k, v, zk, zv, state_k, state_v, cache_k, cache_v, summary, pos, out, ws};
+  const char* names[] = {"q", "k", "v", "zk", "zv", "state_k", "state_v", "cache_k", "cache_v", "summary",
+                         "pos", "out", "ws"};
+  for (int i = 0; i < 13; ++i)
+    if ((st = check_ptr(ptrs[i], names[i], false)) != RAT_OK) return st;
+  if ((st = check_ptr(chosen, "chosen", true)) != RAT_OK) return st;
+  if (ws_bytes < rat_topk_decode_workspace_size())
+    return fail(RAT_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, rat_topk_decode_workspace_size());
+  const bool bf16 = dt == RAT_BF16;
+  uint32_t* hdr = static_cast<uint32_t*>(ws);
+
+  rat::TopkAppendPlan ap;
+  std::memset(&ap, 0, sizeof(ap));
+  ap.k = k; ap.v = v; ap.zk = zk; ap.zv = zv;
+  ap.state_k = state_k; ap.state_v = state_v;
+  ap.cache_k = cache_k; ap.cache_v = cache_v; ap.summary = summary;
+  ap.pos = pos; ap.max_pos = max_pos;
+  ap.B = B; ap.H = H; ap.Dh = Dh; ap.block = block;
+  ap.bf16 = bf16;
+  ap.hdr = hdr;
+  hipError_t e = rat::launch_topk_append(ap, stream);
+  if (e != hipSuccess) return fail(RAT_ERR_HIP, "append launch: %s", hipGetErrorString(e));
+
+  rat::TopkPlan tp;
+  std::memset(&tp, 0, sizeof(tp));
+  tp.q = q; tp.out = out; tp.chosen = chosen;
+  tp.cache_k = cache_k; tp.cache_v = cache_v; tp.summary = summary;
+  tp.pos = pos; tp.max_pos = max_pos;
+  tp.B = B; tp.T = 1; tp.H = H; tp.Dh = Dh; tp.block = block; tp.topk = topk; tp.score = (int)score;
+  tp.bf16 = bf16;
+  tp.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)Dh);
+  tp.hdr = hdr;
+  e = rat::launch_topk_attend(tp, stream);
+  if (e != hipSuccess) return fail(RAT_ERR_HIP, "top-k attention launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -215,4 +215,45 @@ struct DecodePlan {
 };
 hipError_t launch_decode(const DecodePlan& p, hipStream_t s);
 
+// Top-k block attention over a cache of every recurrent state.  The state
+// caches are [H][B][max_pos][Dh] (the grid layout with dilation 1), the
+// block summaries fp32 [H][B][max_pos / block][3][Dh] (min, max, mean of the
+// key states of each complete block).
+constexpr int kTopkMaxBlocks = 8192;   // max_pos / block
+constexpr int kTopkMaxK = 128;
+enum TopkScore { kTopkQuest = 0, kTopkMoba = 1 };
+
+struct TopkPlan {
+  const void* q;        // prefill: [B][T][H][Dh]; decode: [B][H][Dh]
+  void* out;            // same layout as q
+  int32_t* chosen;      // [.. query ..][topk] or null
+  const void* cache_k; const void* cache_v;
+  float* summary;
+  const int32_t* pos;   // decode: device [B]; prefill: null (query row i is position p0 + i)
+  int64_t p0, max_pos;
+  int B, T, H, Dh, block, topk, score;
+  int bf16;
+  float scale;
+  uint32_t* hdr;        // decode: workspace header (error word)
+};
+// Summaries of the blocks j in [j_lo, j_hi) of every (h, b).
+hipError_t launch_topk_stats(const TopkPlan& p, int64_t j_lo, int64_t j_hi, hipStream_t s);
+// Queries (prefill rows or one decode token per sequence): selection and attention.
+hipError_t launch_topk_attend(const TopkPlan& p, hipStream_t s);
+
+struct TopkAppendPlan {
+  const void* k; const void* v;      // [B][H][Dh]
+  const float* zk; const float* zv;
+  float* state_k; float* state_v;    // [B][H][Dh]
+  void* cache_k; void* cache_v;
+  float* summary;
+  const int32_t* pos;
+  int64_t max_pos;
+  int B, H, Dh, block;
+  int bf16;
+  uint32_t* hdr;
+};
+// Decode: state update, cache row at pos[b], summary of a block it completes.
+hipError_t launch_topk_append(const TopkAppendPlan& p, hipStream_t s);
+
 }  // namespace rat

@@ -1,0 +1,349 @@
+// Top-k block attention over RAT+ memory states.
+//
+// "Augmenting Attention with Exponentially Decaying Memory Improves
+// Query-Aware KV Sparsity", section 2.2: query-aware sparse inference scores
+// KV blocks, keeps the best ones and attends only over them; with RAT+ it runs
+// on the memory states (K~, V~).  Block representatives (section 3, sparse
+// inference settings; "RAT+: Train Dense, Infer Sparse", Fig. 3 and Tables
+// 17-18): Quest keeps the dimension-wise min and max of a block's key states
+// and scores sum_d max(q_d min_d, q_d max_d); MoBA keeps their mean and
+// scores q . mean.  The first block and the query's own block are always
+// attended; the top-k complete blocks between them are added (ties to the
+// lower block index).
+//
+// Every recurrent state sits in a cache [H][B][max_pos][Dh]; the summaries
+// of complete blocks in fp32 [H][B][max_pos / block][3][Dh].  One workgroup
+// handles one query: it scores the candidate blocks from the summaries into
+// LDS, takes the top k by repeated block-wide argmax, then streams the rows
+// of the kept blocks (Dh / 8 lanes per row, online softmax per lane group,
+// waves merged in LDS).
+#include "rat_internal.h"
+#include "kv_stream.h"
+
+namespace rat {
+namespace {
+
+constexpr int kAW = 4;        // waves per attend workgroup
+constexpr int kAUnroll = 4;
+
+template <typename ET> __device__ __forceinline__ float ld1(const ET* p);
+template <> __device__ __forceinline__ float ld1<bf16_t>(const bf16_t* p) { return bf16_to_f32(*p); }
+template <> __device__ __forceinline__ float ld1<float>(const float* p) { return *p; }
+template <typename ET> __device__ __forceinline__ void st1(ET* p, float x);
+template <> __device__ __forceinline__ void st1<bf16_t>(bf16_t* p, float x) { *p = bf16_t(pack_bf16x2(x, 0.f) & 0xffffu); }
+template <> __device__ __forceinline__ void st1<float>(float* p, float x) { *p = x; }
+
+__device__ __forceinline__ int64_t cache_off(int B, int64_t max_pos, int h, int b, int64_t row, int Dh) {
+  return (((int64_t)h * B + b) * max_pos + row) * Dh;
+}
+__device__ __forceinline__ int64_t summary_off(int B, int64_t nbcap, int h, int b, int64_t j, int Dh) {
+  return (((int64_t)h * B + b) * nbcap + j) * 3 * Dh;
+}
+
+// ---- summaries of complete blocks: one workgroup of Dh threads per (h, b, j)
+template <typename ET>
+__global__ void topk_stats_kernel(const TopkPlan p, int64_t j_lo, int64_t nj) {
+  const int64_t id = blockIdx.x;
+  const int64_t jj = id % nj;
+  const int64_t hb = id / nj;
+  const int b = int(hb % p.B);
+  const int h = int(hb / p.B);
+  const int64_t j = j_lo + jj;
+  const int d = threadIdx.x;
+  const ET* src = static_cast<const ET*>(p.cache_k) + cache_off(p.B, p.max_pos, h, b, j * p.block, p.Dh) + d;
+  float mn = INFINITY, mx = -INFINITY, sum = 0.f;
+  for (int r = 0; r < p.block; ++r) {
+    const float x = ld1<ET>(src + (int64_t)r * p.Dh);
+    mn = fminf(mn, x);
+    mx = fmaxf(mx, x);
+    sum += x;
+  }
+  float* dst = p.summary + summary_off(p.B, p.max_pos / p.block, h, b, j, p.Dh) + d;
+  dst[0] = mn;
+  dst[p.Dh] = mx;
+  dst[2 * p.Dh] = sum / float(p.block);
+}
+
+// ---- decode: state update, cache row, summary of a block the row completes
+template <typename ET>
+__global__ void topk_append_kernel(const TopkAppendPlan p) {
+  const int bh = blockIdx.x;
+  const int b = bh / p.H;
+  const int h = bh - b * p.H;
+  const int d = threadIdx.x;
+  const int64_t t = p.pos[b];
+  if (t < 0 || t >= p.max_pos) {
+    if (d == 0) atomicOr(&p.hdr[2], kErrDecodePos);
+    return;
+  }
+  const int64_t idx = (int64_t)bh * p.Dh + d;
+  float gk, ck, gv, cv;
+  gate_pair(p.zk[idx], gk, ck);
+  gate_pair(p.zv[idx], gv, cv);
+  const float sk = gk * p.state_k[idx] + ck * ld1<ET>(static_cast<const ET*>(p.k) + idx);
+  const float sv = gv * p.state_v[idx] + cv * ld1<ET>(static_cast<const ET*>(p.v) + idx);
+  p.state_k[idx] = sk;
+  p.state_v[idx] = sv;
+  ET* ck_row = static_cast<ET*>(p.cache_k) + cache_off(p.B, p.max_pos, h, b, t, p.Dh) + d;
+  st1<ET>(ck_row, sk);
+  st1<ET>(static_cast<ET*>(p.cache_v) + cache_off(p.B, p.max_pos, h, b, t, p.Dh) + d, sv);
+  if ((t + 1) % p.block == 0) {
+    // block j = (t+1)/block - 1 is complete: rows before t from the cache,
+    // row t as just stored (rounded to the cache type)
+    const int64_t j = (t + 1) / p.block - 1;
+    const ET* src = static_cast<const ET*>(p.cache_k) + cache_off(p.B, p.max_pos, h, b, j * p.block, p.Dh) + d;
+    float mn = INFINITY, mx = -INFINITY, sum = 0.f;
+    for (int r = 0; r < p.block; ++r) {
+      float x;
+      if (r == p.block - 1) {
+        ET tmp;
+        st1<ET>(&tmp, sk);
+        x = ld1<ET>(&tmp);
+      } else {
+        x = ld1<ET>(src + (int64_t)r * p.Dh);
+      }
+      mn = fminf(mn, x);
+      mx = fmaxf(mx, x);
+      sum += x;
+    }
+    float* dst = p.summary + summary_off(p.B, p.max_pos / p.block, h, b, j, p.Dh) + d;
+    dst[0] = mn;
+    dst[p.Dh] = mx;
+    dst[2 * p.Dh] = sum / float(p.block);
+  }
+}
+
+// better(v, j) than (bv, bi): higher score, ties to the lower index; NaN marks
+// a candidate already taken
+__device__ __forceinline__ bool better(float v, int j, float bv, int bi) {
+  return v == v && (v > bv || (v == bv && j < bi));
+}
+
+// ---- selection and attention: one workgroup per query
+template <typename ET, int DH>
+__global__ __launch_bounds__(kAW * 64) void topk_attend_kernel(const TopkPlan p) {
+  using R = Row8<ET>;
+  constexpr int LPK = DH / 8;      // lanes per row
+  constexpr int KPW = 64 / LPK;    // rows per wave step
+  __shared__ float s_q[DH];
+  __shared__ float s_sc[kTopkMaxBlocks];
+  __shared__ int s_list[kTopkMaxK + 2];
+  __shared__ float s_bv[kAW];
+  __shared__ int s_bi[kAW];
+  __shared__ float s_m[kAW], s_l[kAW];
+  __shared__ float s_acc[kAW][DH];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int rg = lane / LPK;
+  const int c = lane - rg * LPK;
+
+  // ---- the query
+  int b, h;
+  int64_t t, qrow;
+  if (p.pos) {                       // decode: one token per sequence
+    qrow = blockIdx.x;               // b * H + h
+    b = int(qrow / p.H);
+    h = int(qrow - (int64_t)b * p.H);
+    t = p.pos[b];
+  } else {                           // prefill: row (b * T + i) * H + h is position p0 + i
+    qrow = blockIdx.x;
+    h = int(qrow % p.H);
+    const int64_t bi = qrow / p.H;
+    b = int(bi / p.T);
+    t = p.p0 + (bi - (int64_t)b * p.T);
+  }
+  const ET* qp = static_cast<const ET*>(p.q) + qrow * DH;
+  ET* op = static_cast<ET*>(p.out) + qrow * DH;
+  int32_t* cp = p.chosen ? p.chosen + qrow * p.topk : nullptr;
+  if (t < 0 || t >= p.max_pos) {     // decode position out of range: zero row (error bit set by append)
+    if (tid < DH) st1<ET>(op + tid, 0.f);
+    if (cp && tid < p.topk) cp[tid] = -1;
+    return;
+  }
+  if (tid < DH) s_q[tid] = ld1<ET>(qp + tid);
+  __syncthreads();
+
+  const int64_t local = t / p.block;
+  const int ncand = int(local > 1 ? local - 1 : 0);   // candidate blocks 1 .. local-1
+  const int64_t nbcap = p.max_pos / p.block;
+  const float* sb = p.summary + summary_off(p.B, nbcap, h, b, 0, DH);
+
+  // ---- scores of the candidates (score of block j + 1 in s_sc[j])
+  for (int j = tid; j < ncand; j += kAW * 64) {
+    const float* st = sb + (int64_t)(j + 1) * 3 * DH;
+    float s = 0.f;
+    if (p.score == kTopkQuest) {
+#pragma unroll 8
+      for (int d = 0; d < DH; ++d) s += fmaxf(s_q[d] * st[d], s_q[d] * st[DH + d]);
+    } else {
+#pragma unroll 8
+      for (int d = 0; d < DH; ++d) s = fmaf(s_q[d], st[2 * DH + d], s);
+    }
+    s_sc[j] = s == s ? s : -INFINITY;   // NaN marks "taken" below
+  }
+  __syncthreads();
+
+  // ---- the top k (or all candidates when there are at most k)
+  const int nsel = ncand < p.topk ? ncand : p.topk;
+  if (ncand <= p.topk) {
+    for (int j = tid; j < ncand; j += kAW * 64) s_list[1 + j] = j + 1;
+  } else {
+    for (int r = 0; r < nsel; ++r) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+      for (int j = tid; j < ncand; j += kAW * 64) {
+        const float v = s_sc[j];
+        if (better(v, j, bv, bi)) { bv = v; bi = j; }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off);
+        const int oi = __shfl_xor(bi, off);
+        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+      }
+      if (lane == 0) { s_bv[wave] = bv; s_bi[wave] = bi; }
+      __syncthreads();
+      if (tid == 0) {
+        float fv = s_bv[0];
+        int fi = s_bi[0];
+        for (int w = 1; w < kAW; ++w)
+          if (better(s_bv[w], s_bi[w], fv, fi)) { fv = s_bv[w]; fi = s_bi[w]; }
+        s_list[1 + r] = fi + 1;
+        s_sc[fi] = __builtin_nanf("");
+      }
+      __syncthreads();
+    }
+    if (tid == 0) {   // ascending block order
+      for (int i = 2; i <= nsel; ++i) {
+        const int x = s_list[i];
+        int k = i - 1;
+        while (k >= 1 && s_list[k] > x) { s_list[k + 1] = s_list[k]; --k; }
+        s_list[k + 1] = x;
+      }
+    }
+  }
+  __syncthreads();
+  if (cp && tid < p.topk) cp[tid] = tid < nsel ? s_list[1 + tid] : -1;
+
+  // ---- key blocks: first, chosen, local (block 0 alone when local == 0)
+  const int nlist = local > 0 ? nsel + 2 : 1;
+  auto list_block = [&](int e) -> int64_t {
+    if (local == 0) return 0;
+    if (e == 0) return 0;
+    if (e == nlist - 1) return local;
+    return s_list[e];
+  };
+
+  float q8[8];
+  const float sl2 = p.scale * 1.4426950408889634f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q8[i] = s_q[8 * c + i] * sl2;
+  Soft sm;
+  sm.m = -INFINITY;
+  sm.l = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sm.acc[i] = 0.f;
+
+  const ET* kc = static_cast<const ET*>(p.cache_k) + cache_off(p.B, p.max_pos, h, b, 0, DH) + 8 * c;
+  const ET* vc = static_cast<const ET*>(p.cache_v) + cache_off(p.B, p.max_pos, h, b, 0, DH) + 8 * c;
+  for (int e = wave; e < nlist; e += kAW) {
+    const int64_t blk = list_block(e);
+    const int64_t r_lo = blk * p.block;
+    const int64_t r_hi = min(r_lo + p.block, t + 1);   // the local block stops at t
+    for (int64_t base = r_lo; base < r_hi; base += KPW * kAUnroll) {
+      typename R::raw kr[kAUnroll], vr[kAUnroll];
+#pragma unroll
+      for (int u = 0; u < kAUnroll; ++u) {
+        const int64_t r = base + u * KPW + rg;
+        const bool ok = r < r_hi;
+        kr[u] = ok ? R::load(kc + r * DH) : R::zero();
+        vr[u] = ok ? R::load(vc + r * DH) : R::zero();
+      }
+      float sc[kAUnroll];
+      float vv[kAUnroll][8];
+#pragma unroll
+      for (int u = 0; u < kAUnroll; ++u) {
+        float kf[8];
+        R::get(kr[u], kf);
+        R::get(vr[u], vv[u]);
+        float d0 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d0 = fmaf(q8[i], kf[i], d0);
+        d0 = group_sum<LPK>(d0);
+        sc[u] = (base + u * KPW + rg) < r_hi ? d0 : -INFINITY;
+      }
+      soft_update<kAUnroll>(sm, sc, vv);
+    }
+  }
+
+  // ---- merge the lane groups of a wave, then the waves
+#pragma unroll
+  for (int off = LPK; off < 64; off <<= 1) {
+    const float m2 = __shfl_xor(sm.m, off);
+    const float l2 = __shfl_xor(sm.l, off);
+    float a2[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a2[i] = __shfl_xor(sm.acc[i], off);
+    soft_merge(sm, m2, l2, a2);
+  }
+  if (rg == 0) {
+    if (c == 0) { s_m[wave] = sm.m; s_l[wave] = sm.l; }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s_acc[wave][8 * c + i] = sm.acc[i];
+  }
+  __syncthreads();
+  if (wave == 0 && rg == 0) {
+    Soft fin;
+    fin.m = s_m[0];
+    fin.l = s_l[0];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) fin.acc[i] = s_acc[0][8 * c + i];
+#pragma unroll
+    for (int w = 1; w < kAW; ++w) soft_merge(fin, s_m[w], s_l[w], &s_acc[w][8 * c]);
+    const float inv = fin.l > 0.f ? 1.0f / fin.l : 0.f;
+    float o8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o8[i] = fin.acc[i] * inv;
+    R::store(op + 8 * c, o8);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_topk_stats(const TopkPlan& p, int64_t j_lo, int64_t j_hi, hipStream_t s) {
+  const int64_t nj = j_hi - j_lo;
+  if (nj <= 0) return hipSuccess;
+  const int64_t blocks = (int64_t)p.H * p.B * nj;
+  if (p.bf16)
+    hipLaunchKernelGGL(topk_stats_kernel<bf16_t>, dim3((unsigned)blocks), dim3(p.Dh), 0, s, p, j_lo, nj);
+  else
+    hipLaunchKernelGGL(topk_stats_kernel<float>, dim3((unsigned)blocks), dim3(p.Dh), 0, s, p, j_lo, nj);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_append(const TopkAppendPlan& p, hipStream_t s) {
+  const int blocks = p.B * p.H;
+  if (p.bf16)
+    hipLaunchKernelGGL(topk_append_kernel<bf16_t>, dim3(blocks), dim3(p.Dh), 0, s, p);
+  else
+    hipLaunchKernelGGL(topk_append_kernel<float>, dim3(blocks), dim3(p.Dh), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_attend(const TopkPlan& p, hipStream_t s) {
+  const int64_t blocks = p.pos ? (int64_t)p.B * p.H : (int64_t)p.B * p.T * p.H;
+  if (blocks <= 0) return hipSuccess;
+  const dim3 grid((unsigned)blocks), threads(kAW * 64);
+  if (p.bf16) {
+    if (p.Dh == 128) hipLaunchKernelGGL((topk_attend_kernel<bf16_t, 128>), grid, threads, 0, s, p);
+    else hipLaunchKernelGGL((topk_attend_kernel<bf16_t, 64>), grid, threads, 0, s, p);
+  } else {
+    if (p.Dh == 128) hipLaunchKernelGGL((topk_attend_kernel<float, 128>), grid, threads, 0, s, p);
+    else hipLaunchKernelGGL((topk_attend_kernel<float, 64>), grid, threads, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace rat

@@ -143,3 +143,35 @@ def test_prefill_chunk_workspace_size():
     c = R.rat_prefill_chunk_workspace_size(1, 1024, 16, 128, 16, 128, 4096)
     assert 0 < a < b < c          # window buffers; later chunks also hold the ring prefix and more grid
     assert R.rat_prefill_chunk_workspace_size(1, 1024, 16, 128, 16, 0, -64) == 0
+
+
+def test_topk_validation():
+    L = R.lib()
+
+    def pre(block=64, topk=8, score=0, p0=0, T=256, max_pos=1024, chosen=None, q=FAKE, wsb=0):
+        return L.rat_topk_prefill(q, FAKE, FAKE, FAKE, FAKE, FAKE, chosen, FAKE, FAKE, FAKE, FAKE, FAKE, p0,
+                                  max_pos, 1, T, 2, 128, block, topk, score, -1.0, 1, FAKE, wsb, None)
+
+    assert pre(block=0) == -1
+    assert pre(block=2048) == -1
+    assert pre(topk=-1) == -1
+    assert pre(topk=129) == -1
+    assert pre(score=5) == -1
+    assert pre(p0=-1) == -1
+    assert pre(T=1025) == -1                  # p0 + T > max_pos
+    assert pre(block=1, max_pos=8193) == -2   # more blocks than a workgroup can score
+    assert pre(q=None) == -1
+    assert pre(chosen=MIS) == -1
+    assert pre() == -3                        # workspace too small
+    assert pre(T=0, q=None) == 0
+
+    def dec(block=64, topk=8, pos=FAKE, wsb=0, max_pos=1024):
+        return L.rat_topk_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, pos, max_pos, FAKE,
+                                      None, 2, 2, 64, block, topk, 1, -1.0, 1, FAKE, wsb, None)
+
+    assert dec(block=0) == -1
+    assert dec(pos=None) == -1
+    assert dec(max_pos=0) == -1
+    assert dec() == -3
+    assert L.rat_topk_decode_workspace_size() == 256
+    assert R.lib().rat_topk_prefill_workspace_size(1, 4096, 16, 128) > 256

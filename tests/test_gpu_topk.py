@@ -1,0 +1,169 @@
+"""Top-k block attention over the memory states (rat_topk_prefill,
+rat_topk_decode_step) against the fp64 oracle (oracle.topk_oracle).
+
+The block choice is a floating-point decision: the kernel scores in fp32, the
+oracle in fp64, so near-ties may fall either way.  Each test therefore checks
+that the kernel's choice is a valid top-k under the oracle's scores (every
+chosen block scores at least as high as every unchosen candidate, up to a
+bound on the fp32 rounding of the two scores), compares the outputs with the
+oracle's attention over the kernel's own choice, and requires the choice to
+equal the oracle's own for almost every query.  Caches and block summaries
+are compared with the oracle's states and statistics."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import topk_oracle as TK
+from recurrence_augmented_dilated_amd import inputs
+from tests.gpu_util import BF16_TOL, F32_TOL, f64, need_gpu, report
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+METHODS = {0: TK.QUEST, 1: TK.MOBA}
+
+
+def _check_choice(sel_row, q_row, kmin, kmax, kmean, t, block, topk, method):
+    """sel_row: the kernel's chosen blocks (-1 padded) for one query; stats
+    [nb, Dh] of its (b, h), taken over the states rounded to the cache type
+    (the precision the kernel decides in).  Returns (choice, equal to the
+    oracle's)."""
+    local = t // block
+    cand = list(range(1, local))
+    sel = [int(x) for x in sel_row if x >= 0]
+    assert all(x == -1 for x in sel_row[len(sel):]), sel_row
+    assert sel == sorted(set(sel)) and all(1 <= j < local for j in sel), (t, sel)
+    assert len(sel) == min(topk, len(cand)), (t, sel, topk, len(cand))
+    scores = {j: TK.block_score(q_row, kmin[j], kmax[j], kmean[j], method) for j in cand}
+    if method == TK.QUEST:
+        bound = {j: float(np.sum(np.abs(q_row) * np.maximum(np.abs(kmin[j]), np.abs(kmax[j])))) for j in cand}
+    else:
+        bound = {j: float(np.sum(np.abs(q_row) * np.abs(kmean[j]))) + float(np.sum(np.abs(q_row))) * 0.02 for j in cand}
+    # fp32 scoring, plus one state element rounded the other way at a
+    # rounding boundary (fp32 vs fp64 recurrence)
+    flip = {j: float(np.max(np.abs(q_row) * np.maximum(np.abs(kmin[j]), np.abs(kmax[j])))) * 2.0 ** -7 for j in cand}
+    eps = {j: 2e-5 * bound[j] + flip[j] + 1e-6 for j in cand}
+    for c in sel:
+        for u in set(cand) - set(sel):
+            assert scores[c] >= scores[u] - (eps[c] + eps[u]), (t, c, u, scores[c], scores[u])
+    return sel, sel == TK.select_blocks(t, block, topk, [scores.get(j, -np.inf) for j in range(max(local, 1))])
+
+
+def _verify(out, chosen, q, Kt, Vt, t_list, block, topk, method, tol, stats, what):
+    """out/chosen: GPU results for queries (b, t, h) -> rows; checks choice and output."""
+    agree = total = 0
+    worst = 0.0
+    kmin, kmax, kmean = stats
+    scale = oracle.default_scale(q.shape[-1])
+    for (b, t, h), (o_row, s_row) in zip(t_list, zip(out, chosen)):
+        sel, same = _check_choice(s_row, q[b, t, h], kmin[b, :, h], kmax[b, :, h], kmean[b, :, h], t, block, topk,
+                                  method)
+        want = TK.attend_selected(q[b, t, h], Kt[b, :, h], Vt[b, :, h], t, block, sel, scale)
+        worst = max(worst, float(np.max(np.abs(o_row - want))))
+        agree += same
+        total += 1
+    print(f"[topk] {what}: max_abs={worst:.3e}, choice equal to the oracle's for {agree}/{total}", flush=True)
+    assert worst <= tol, what
+    assert agree >= 0.97 * total, (agree, total)
+
+
+def _run(B, H, Dh, block, topk, score, chunks, decode_steps, dtype, seed, mu=1.5):
+    R = need_gpu()
+    tol = BF16_TOL if dtype == torch.bfloat16 else F32_TOL
+    method = METHODS[score]
+    L = sum(chunks)
+    total = L + decode_steps
+    max_pos = (total + block - 1) // block * block + block
+    print(f"[topk] B={B} H={H} Dh={Dh} block={block} topk={topk} {method} chunks={chunks} decode={decode_steps} "
+          f"{dtype}", flush=True)
+    x = inputs.prefill_inputs(B, total, H, Dh, dtype=dtype, mu=mu, seed=seed)
+    q = f64(x["q"])
+    Kt = oracle.scan(f64(x["k"]), f64(x["zk"]))
+    Vt = oracle.scan(f64(x["v"]), f64(x["zv"]))
+    Kr = torch.from_numpy(Kt).to(dtype).double().numpy()   # states as the cache stores them
+    cache = R.topk_cache(B, H, Dh, max_pos, block, dtype, DEV)
+    p0 = 0
+    for T in chunks:
+        sl = slice(p0, p0 + T)
+        d = {n: t[:, sl].contiguous().to(DEV) for n, t in x.items()}
+        chosen = torch.full((B, T, H, max(topk, 1)), -7, dtype=torch.int32, device=DEV)
+        out = R.rat_topk_prefill(d["q"], d["k"], d["v"], d["zk"], d["zv"], cache, p0, max_pos, block, topk, score,
+                                 chosen=chosen if topk > 0 else None)
+        torch.cuda.synchronize()
+        stats = TK.block_stats(Kr[:, :p0 + T], block)
+        keys = [(b, p0 + i, h) for b in range(B) for i in range(T) for h in range(H)]
+        o = f64(out).reshape(B * T * H, Dh)
+        c = chosen.cpu().numpy().reshape(B * T * H, -1) if topk > 0 else np.full((B * T * H, 1), -1)
+        _verify(o, c[:, :topk] if topk > 0 else np.zeros((B * T * H, 0), dtype=int), q, Kt, Vt, keys, block, topk,
+                method, tol, stats, f"prefill p0={p0} T={T}")
+        p0 += T
+    # caches and summaries after the prefix
+    ck = f64(cache["cache_k"])            # [H, B, max_pos, Dh]
+    for h in range(H):
+        assert np.max(np.abs(ck[h, :, :L] - Kt[:, :L, h])) <= tol
+        assert np.max(np.abs(f64(cache["cache_v"])[h, :, :L] - Vt[:, :L, h])) <= tol
+    smin, smax, smean = TK.block_stats(Kt[:, :L], block)
+    summ = f64(cache["summary"])         # [H, B, nb, 3, Dh]
+    nb = L // block
+    for h in range(H):
+        for s_i, ref in enumerate((smin, smax, smean)):
+            assert np.max(np.abs(summ[h, :, :nb, s_i] - ref[:, :nb, h]), initial=0.0) <= tol
+    assert np.max(np.abs(f64(cache["state_k"]) - Kt[:, L - 1])) <= 1e-4
+    # decode on
+    pos = torch.full((B,), L, dtype=torch.int32, device=DEV)
+    outs, chs, keys = [], [], []
+    for i in range(decode_steps):
+        t = L + i
+        d = {n: x[n][:, t].contiguous().to(DEV) for n in x}
+        chosen = torch.full((B, H, max(topk, 1)), -7, dtype=torch.int32, device=DEV)
+        o = R.rat_topk_decode_step(d["q"], d["k"], d["v"], d["zk"], d["zv"], cache, pos, max_pos, block, topk,
+                                   score, chosen=chosen if topk > 0 else None)
+        torch.cuda.synchronize()
+        outs.append(f64(o).reshape(B * H, Dh))
+        chs.append(chosen.cpu().numpy().reshape(B * H, -1)[:, :topk])
+        keys += [(b, t, h) for b in range(B) for h in range(H)]
+        pos += 1
+    if decode_steps:
+        stats = TK.block_stats(Kr, block)
+        _verify(np.concatenate(outs), np.concatenate(chs), q, Kt, Vt, keys, block, topk, method, tol, stats, "decode")
+
+
+@pytest.mark.parametrize("score", [0, 1], ids=["quest", "moba"])
+def test_topk_prefill_bf16(score):
+    _run(2, 2, 128, 64, 4, score, [1024], 0, torch.bfloat16, seed=31)
+
+
+@pytest.mark.parametrize("score", [0, 1], ids=["quest", "moba"])
+def test_topk_chunks_then_decode(score):
+    """Chunks not aligned to blocks, then decode steps that complete blocks."""
+    _run(1, 3, 64, 32, 3, score, [300, 200], 70, torch.bfloat16, seed=32)
+
+
+def test_topk_fp32():
+    _run(1, 2, 64, 16, 2, 0, [160, 96], 40, torch.float32, seed=33)
+
+
+@pytest.mark.parametrize("topk", [0, 100])
+def test_topk_degenerate_budgets(topk):
+    """topk = 0: first + local block only; topk above the candidate count: every block."""
+    _run(1, 2, 128, 32, topk, 1, [256], 20, torch.bfloat16, seed=34)
+
+
+def test_topk_block_of_one():
+    _run(1, 1, 64, 1, 5, 0, [48], 16, torch.bfloat16, seed=35)
+
+
+def test_topk_decode_bad_position():
+    R = need_gpu()
+    B, H, Dh, block, max_pos = 2, 2, 64, 16, 128
+    cache = R.topk_cache(B, H, Dh, max_pos, block, torch.bfloat16, DEV)
+    st = inputs.decode_step_inputs(B, H, Dh, 1, seed=3, device=DEV)
+    ws = torch.zeros(R.lib().rat_topk_decode_workspace_size(), dtype=torch.uint8, device=DEV)
+    pos = torch.tensor([5, max_pos], dtype=torch.int32, device=DEV)
+    out = R.rat_topk_decode_step(st["q"][0], st["k"][0], st["v"][0], st["zk"][0], st["zv"][0], cache, pos, max_pos,
+                                 block, 2, 0, ws=ws)
+    torch.cuda.synchronize()
+    assert R.workspace_error(ws) & 2
+    assert torch.all(out[1] == 0)
+    assert torch.all(cache["cache_k"][:, 1] == 0)     # the bad sequence's cache is untouched
+    assert torch.any(cache["cache_k"][:, 0, 5] != 0)
