@@ -7,3 +7,4 @@ from .rat_oracle import (  # noqa: F401
     DecodeCache, attend, default_scale, gates, key_set, pairs, prefill, scan,
 )
 from . import topk_oracle  # noqa: F401,E402
+from . import local_oracle  # noqa: F401,E402

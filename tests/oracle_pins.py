@@ -544,3 +544,78 @@ def run_topk(T):
         except Exception as e:  # noqa: BLE001
             failed.append(f"{p.__name__}: {type(e).__name__}: {e}")
     return failed
+
+
+# ---------------------------------------------------------------------------
+# RAT chunk-local variant (oracle.local_oracle)
+# ---------------------------------------------------------------------------
+
+def lpin_chunks_are_independent(LO):
+    """The chunk-local states are the RAT+ recurrence run on every chunk
+    separately from a zero state."""
+    import oracle.rat_oracle as O
+    rng = _rng(41)
+    x = rng.normal(size=(2, 50, 2, 3))
+    z = rng.normal(1, 1.5, size=x.shape)
+    for L in (1, 4, 7, 50, 64):
+        want = np.concatenate([O.scan(x[:, s:s + L], z[:, s:s + L]) for s in range(0, 50, L)], axis=1)
+        _close(LO.scan_local(x, z, L), want, 1e-13, f"chunk-local states L={L}")
+
+
+def lpin_full_chunk_is_ratplus(LO):
+    """L = T is the RAT+ recurrence, and the operator equals RAT+ with D = T, W = 1."""
+    import oracle.rat_oracle as O
+    rng = _rng(42)
+    q, k, v = (rng.normal(size=(1, 30, 2, 4)) for _ in range(3))
+    zk, zv = rng.normal(1, 1, size=(2, 1, 30, 2, 4))
+    _close(LO.scan_local(k, zk, 30), O.scan(k, zk), 1e-14, "L = T states")
+    _close(LO.local_prefill(q, k, v, zk, zv, 30), O.prefill(q, k, v, zk, zv, 30, 1), 1e-13, "L = T operator")
+
+
+def lpin_unit_chunks_are_causal_attention(LO):
+    """L = 1 with open gates (z = -inf, so g = 0) leaves the raw keys and
+    values as states, every earlier chunk-final state is a key: causal
+    softmax attention (torch sdpa on the CPU, fp64)."""
+    rng = _rng(43)
+    B, T, H, Dh = 1, 24, 2, 8
+    q, k, v = (rng.normal(size=(B, T, H, Dh)) for _ in range(3))
+    z = np.full((B, T, H, Dh), -np.inf)
+    _close(LO.local_prefill(q, k, v, z, z, 1), _sdpa_causal(q, k, v, 1.0 / math.sqrt(Dh)), 1e-12,
+           "L = 1, g = 0 == causal attention")
+
+
+def lpin_key_positions(LO):
+    for L in (1, 3, 8):
+        for t in range(40):
+            want = [p for p in range(t) if (p + 1) % L == 0 and p < (t // L) * L] + [t]
+            assert list(LO.key_positions(t, L)) == want, (L, t)
+
+
+def lpin_decode_continuation(LO):
+    """Prefill of T + s positions equals prefill of T, then s decode steps
+    from the chunk-local cache (steps cross chunk starts)."""
+    rng = _rng(44)
+    B, H, Dh, L, T, s = 2, 2, 4, 5, 13, 9
+    q, k, v = (rng.normal(size=(B, T + s, H, Dh)) for _ in range(3))
+    zk, zv = rng.normal(1, 1, size=(2, B, T + s, H, Dh))
+    full = LO.local_prefill(q, k, v, zk, zv, L)
+    cap = [(T + s) // L] * H
+    cache = LO.local_cache_from_prefill(k[:, :T], v[:, :T], zk[:, :T], zv[:, :T], L, cap)
+    for i in range(s):
+        t = T + i
+        out = LO.local_decode_step(cache, q[:, t], k[:, t], v[:, t], zk[:, t], zv[:, t], [t] * B, L)
+        _close(out, full[:, t], 1e-12, f"decode step at {t}")
+
+
+LOCAL_PINS = [lpin_chunks_are_independent, lpin_full_chunk_is_ratplus, lpin_unit_chunks_are_causal_attention,
+              lpin_key_positions, lpin_decode_continuation]
+
+
+def run_local(LO):
+    failed = []
+    for p in LOCAL_PINS:
+        try:
+            p(LO)
+        except Exception as e:  # noqa: BLE001
+            failed.append(f"{p.__name__}: {type(e).__name__}: {e}")
+    return failed

@@ -126,3 +126,40 @@ def test_topk_mutant_is_caught(name):
     old, new = TOPK_MUTANTS[name]
     failed = oracle_pins.run_topk(_topk_mutant(old, new))
     assert failed, f"no pin catches the mutant: {name}"
+
+
+# RAT chunk-local oracle (oracle/local_oracle.py) against its own pins
+import oracle.local_oracle as real_local  # noqa: E402
+
+LOCAL_MUTANTS = {
+    "restart one position late": ("if t % L == 0:\n            h = np.zeros", "if t % L == 1:\n            h = np.zeros"),
+    "no restart": ("if t % L == 0:\n            h = np.zeros", "if False:\n            h = np.zeros"),
+    "chunk starts from the raw input (gate forced shut)": (
+        "        g, c = gates(z[:, t])\n        h = g * h + c * x[:, t]",
+        "        g, c = gates(z[:, t])\n        h = x[:, t] if t % L == 0 else g * h + c * x[:, t]"),
+    "own state not attended": ("return key_set(t, L, 1)", "return key_set(t, L, 0)"),
+    "chunk keys one chunk apart": ("return prefill(q, None, None, None, None, L, 1,",
+                                   "return prefill(q, None, None, None, None, L + 1, 1,"),
+    "decode does not restart at chunk starts": ("if int(t) % L == 0:\n            cache.state_k[b] = 0.0",
+                                                "if False:\n            cache.state_k[b] = 0.0"),
+}
+
+
+def _local_mutant(old, new):
+    src = inspect.getsource(real_local)
+    assert src.count(old) >= 1, f"mutation site not found: {old!r}"
+    src = src.replace(old, new).replace("from .rat_oracle import", "from oracle.rat_oracle import")
+    mod = types.ModuleType("local_mutant")
+    exec(compile(src, "local_mutant", "exec"), mod.__dict__)  # noqa: S102
+    return mod
+
+
+def test_real_local_oracle_passes_every_pin():
+    assert oracle_pins.run_local(real_local) == []
+
+
+@pytest.mark.parametrize("name", list(LOCAL_MUTANTS))
+def test_local_mutant_is_caught(name):
+    old, new = LOCAL_MUTANTS[name]
+    failed = oracle_pins.run_local(_local_mutant(old, new))
+    assert failed, f"no pin catches the mutant: {name}"

@@ -13,3 +13,8 @@ def test_pin(pin):
 @pytest.mark.parametrize("pin", oracle_pins.TOPK_PINS, ids=lambda p: p.__name__)
 def test_topk_pin(pin):
     pin(oracle.topk_oracle)
+
+
+@pytest.mark.parametrize("pin", oracle_pins.LOCAL_PINS, ids=lambda p: p.__name__)
+def test_local_pin(pin):
+    pin(oracle.local_oracle)
