@@ -232,6 +232,34 @@ rat_status_t rat_decode_step(const void* q, const void* k, const void* v, const 
                              void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
+ * RAT's chunk-local variant ("RAT: Bridging RNN Efficiency and Attention
+ * Accuracy via Chunk-based Sequence Modeling", approach): the recurrence runs
+ * inside chunks of L positions, restarting from a zero state at every
+ * position j with j mod L == 0 (L = T is the RAT+ recurrence, RAT+ Fig. 1a),
+ * and each query attends over the final states of the earlier chunks plus
+ * its own state: the RAT+ key set with D = L and W = 1.  The arguments are
+ * those of rat_prefill_chunk / rat_decode_step with dilation L on every head
+ * and W = 1 (ring_k/_v [B][H][1][Dh]; grid layout rat_grid_layout(H, L...));
+ * L >= 1.
+ * ------------------------------------------------------------------------ */
+size_t rat_local_prefill_chunk_workspace_size(int32_t B, int32_t T, int32_t H, int32_t Dh, int32_t L,
+                                              int64_t p0, rat_dtype_t dtype);
+rat_status_t rat_local_prefill_chunk(const void* q, const void* k, const void* v, const float* zk,
+                                     const float* zv, void* out, float* state_k, float* state_v,
+                                     void* grid_k, void* grid_v, const int64_t* grid_off,
+                                     const int32_t* grid_cap, void* ring_k, void* ring_v, int64_t p0,
+                                     int64_t max_pos, int32_t B, int32_t T, int32_t H, int32_t Dh,
+                                     int32_t L, float scale, rat_dtype_t dtype, void* ws,
+                                     size_t ws_bytes, hipStream_t stream);
+size_t rat_local_decode_workspace_size(int32_t B, int32_t H, int32_t Dh, int32_t L, int64_t max_pos);
+rat_status_t rat_local_decode_step(const void* q, const void* k, const void* v, const float* zk,
+                                   const float* zv, float* state_k, float* state_v, void* grid_k,
+                                   void* grid_v, const int64_t* grid_off, const int32_t* grid_cap,
+                                   void* ring_k, void* ring_v, const int32_t* pos, int64_t max_pos,
+                                   void* out, int32_t B, int32_t H, int32_t Dh, int32_t L, float scale,
+                                   rat_dtype_t dtype, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
  * Top-k block attention over the memory states ("Augmenting Attention with
  * Exponentially Decaying Memory Improves Query-Aware KV Sparsity", sections
  * 2.2 and 3; RAT+ Fig. 3 and Tables 17-18).  Positions are cut into blocks of

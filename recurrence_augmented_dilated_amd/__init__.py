@@ -93,6 +93,17 @@ def lib():
             L.rat_topk_decode_step.restype = c_int
             L.rat_topk_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, c_i64, vp, vp, c_int,
                                                c_int, c_int, c_int, c_int, c_int, c_f, c_int, vp, c_sz, vp]
+            L.rat_local_prefill_chunk_workspace_size.restype = c_sz
+            L.rat_local_prefill_chunk_workspace_size.argtypes = [c_int, c_int, c_int, c_int, c_int, c_i64, c_int]
+            L.rat_local_prefill_chunk.restype = c_int
+            L.rat_local_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, c_i64,
+                                                  c_i64, c_int, c_int, c_int, c_int, c_int, c_f, c_int, vp, c_sz,
+                                                  vp]
+            L.rat_local_decode_workspace_size.restype = c_sz
+            L.rat_local_decode_workspace_size.argtypes = [c_int, c_int, c_int, c_int, c_i64]
+            L.rat_local_decode_step.restype = c_int
+            L.rat_local_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, c_i64, vp,
+                                                c_int, c_int, c_int, c_int, c_f, c_int, vp, c_sz, vp]
             _lib = L
     return _lib
 
@@ -299,6 +310,51 @@ def rat_prefill_chunk(q, k, v, zk, zv, state_k, state_v, grid_k, grid_v, grid_of
         _ptr(q), _ptr(k), _ptr(v), _ptr(zk), _ptr(zv), _ptr(out), _ptr(state_k), _ptr(state_v),
         _ptr(grid_k), _ptr(grid_v), off, cap, _ptr(ring_k), _ptr(ring_v), int(p0), int(max_pos), B, T, H,
         Dh, _i32_array(dil), int(W), s, _dtype_code(q), _ptr(ws), ws.numel(), _stream(q.device)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# RAT chunk-local variant (restart every L positions, D = L, W = 1)
+# ---------------------------------------------------------------------------
+
+def rat_local_prefill_chunk(q, k, v, zk, zv, state_k, state_v, grid_k, grid_v, grid_off, grid_cap, ring_k,
+                            ring_v, p0, max_pos, L, scale=None, out=None, ws=None):
+    """Chunk-local prefill of positions p0 .. p0+T-1 continuing a decode
+    cache (grid layout rat_grid_layout(H, L, max_pos), ring [B, H, 1, Dh])."""
+    B, T, H, Dh = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if ws is None:
+        n = int(lib().rat_local_prefill_chunk_workspace_size(B, T, H, Dh, int(L), int(p0), _dtype_code(q)))
+        ws = workspace(n, q.device, "local_chunk")
+    off = (ctypes.c_int64 * H)(*[int(x) for x in grid_off])
+    cap = _i32_array(grid_cap)
+    s = -1.0 if scale is None else float(scale)
+    _check(lib().rat_local_prefill_chunk(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(zk), _ptr(zv), _ptr(out), _ptr(state_k), _ptr(state_v), _ptr(grid_k),
+        _ptr(grid_v), off, cap, _ptr(ring_k), _ptr(ring_v), int(p0), int(max_pos), B, T, H, Dh, int(L), s,
+        _dtype_code(q), _ptr(ws), ws.numel(), _stream(q.device)))
+    return out
+
+
+def rat_local_decode_step(q, k, v, zk, zv, state_k, state_v, grid_k, grid_v, grid_off, grid_cap, ring_k, ring_v,
+                          pos, max_pos, L, scale=None, out=None, ws=None):
+    """One chunk-local decode step at positions pos (int32 [B])."""
+    B, H, Dh = q.shape
+    if pos.dtype != torch.int32:
+        raise TypeError("pos must be int32")
+    if out is None:
+        out = torch.empty_like(q)
+    if ws is None:
+        ws = workspace(int(lib().rat_local_decode_workspace_size(B, H, Dh, int(L), int(max_pos))), q.device,
+                       "local_decode")
+    off = (ctypes.c_int64 * H)(*[int(x) for x in grid_off])
+    cap = _i32_array(grid_cap)
+    s = -1.0 if scale is None else float(scale)
+    _check(lib().rat_local_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(zk), _ptr(zv), _ptr(state_k), _ptr(state_v), _ptr(grid_k), _ptr(grid_v),
+        off, cap, _ptr(ring_k), _ptr(ring_v), _ptr(pos), int(max_pos), _ptr(out), B, H, Dh, int(L), s,
+        _dtype_code(q), _ptr(ws), ws.numel(), _stream(q.device)))
     return out
 
 

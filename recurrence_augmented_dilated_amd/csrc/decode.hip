@@ -42,6 +42,7 @@ struct DecArgs {
   uint32_t* hdr;
   int B, H, W, max_split;
   float sl2;
+  int reset_every;
   DecodeHeads heads;
 };
 
@@ -89,8 +90,10 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(const DecArgs a) {
                                      : static_cast<const float*>(a.k)[idx];
     const float xv = sizeof(ET) == 2 ? bf16_to_f32(static_cast<const bf16_t*>(a.v)[idx])
                                      : static_cast<const float*>(a.v)[idx];
-    const float sk = gk * a.state_k[idx] + ck * xk;
-    const float sv = gv * a.state_v[idx] + cv * xv;
+    // chunk-local recurrence: a position that starts a chunk drops the carried state
+    const bool restart = a.reset_every > 0 && t % a.reset_every == 0;
+    const float sk = (restart ? 0.f : gk * a.state_k[idx]) + ck * xk;
+    const float sv = (restart ? 0.f : gv * a.state_v[idx]) + cv * xv;
     a.state_k[idx] = sk;
     a.state_v[idx] = sv;
     const float rk = R::round(sk);
@@ -283,6 +286,7 @@ hipError_t launch_decode(const DecodePlan& p, hipStream_t s) {
   a.partials = p.partials; a.hdr = p.hdr;
   a.B = p.B; a.H = p.H; a.W = p.W; a.max_split = p.max_split;
   a.sl2 = p.scale * 1.4426950408889634f;
+  a.reset_every = p.reset_every;
   a.heads = p.heads;
   if (p.bf16) {
     return p.Dh == 128 ? launch_typed<bf16_t, 128>(a, p.n_items, p.any_split, s)

@@ -321,13 +321,13 @@ size_t rat_prefill_chunk_workspace_size(int32_t B, int32_t T, int32_t H, int32_t
   return chunk_carve(B, T, H, Dh, dilation, W, p0, dt).total;
 }
 
-rat_status_t rat_prefill_chunk(const void* q, const void* k, const void* v, const float* zk,
+static rat_status_t prefill_chunk_impl(const void* q, const void* k, const void* v, const float* zk,
                                const float* zv, void* out, float* state_k, float* state_v,
                                void* grid_k, void* grid_v, const int64_t* grid_off,
                                const int32_t* grid_cap, void* ring_k, void* ring_v, int64_t p0,
                                int64_t max_pos, int32_t B, int32_t T, int32_t H, int32_t Dh,
                                const int32_t* dilation, int32_t W, float scale, rat_dtype_t dt,
-                               void* ws, size_t ws_bytes, hipStream_t stream) {
+                               void* ws, size_t ws_bytes, hipStream_t stream, int32_t reset_every) {
   rat_status_t st = check_common(B, T, H, Dh, dt);
   if (st != RAT_OK) return st;
   if (W < 0) return fail(RAT_ERR_INVALID_ARG, "W must be >= 0 (got %d)", W);
@@ -411,6 +411,7 @@ rat_status_t rat_prefill_chunk(const void* q, const void* k, const void* v, cons
   sp.arows = cv.arows;
   sp.W = W;
   sp.ring_from = std::max<int64_t>(p0, p0 + T - W);
+  sp.reset_every = reset_every;
   sp.bf16 = bf16;
   sp.heads = cache;
   sp.ws = ws;
@@ -458,6 +459,16 @@ rat_status_t rat_prefill_chunk(const void* q, const void* k, const void* v, cons
   return ok();
 }
 
+rat_status_t rat_prefill_chunk(const void* q, const void* k, const void* v, const float* zk,
+                               const float* zv, void* out, float* state_k, float* state_v,
+                               void* grid_k, void* grid_v, const int64_t* grid_off,
+                               const int32_t* grid_cap, void* ring_k, void* ring_v, int64_t p0,
+                               int64_t max_pos, int32_t B, int32_t T, int32_t H, int32_t Dh,
+                               const int32_t* dilation, int32_t W, float scale, rat_dtype_t dt,
+                               void* ws, size_t ws_bytes, hipStream_t stream) {  return prefill_chunk_impl(q, k, v, zk, zv, out, state_k, state_v, grid_k, grid_v, grid_off, grid_cap, ring_k,
+                            ring_v, p0, max_pos, B, T, H, Dh, dilation, W, scale, dt, ws, ws_bytes, stream, 0);
+}
+
 // ---------------------------------------------------------------------------
 rat_status_t rat_grid_layout(int32_t H, const int32_t* dilation, int64_t max_pos, int64_t* grid_off,
                              int32_t* grid_cap, int64_t* rows) {
@@ -489,13 +500,13 @@ size_t rat_decode_workspace_size(int32_t B, int32_t H, int32_t Dh, const int32_t
   return sizeof(rat::WsHeader) + align_up((size_t)B * H * max_split * (Dh + 2) * sizeof(float));
 }
 
-rat_status_t rat_decode_step(const void* q, const void* k, const void* v, const float* zk,
+static rat_status_t decode_step_impl(const void* q, const void* k, const void* v, const float* zk,
                              const float* zv, float* state_k, float* state_v, void* grid_k,
                              void* grid_v, const int64_t* grid_off, const int32_t* grid_cap,
                              void* ring_k, void* ring_v, const int32_t* pos, int64_t max_pos,
                              void* out, int32_t B, int32_t H, int32_t Dh, const int32_t* dilation,
                              int32_t W, float scale, rat_dtype_t dt, void* ws, size_t ws_bytes,
-                             hipStream_t stream) {
+                             hipStream_t stream, int32_t reset_every) {
   rat_status_t st = check_common(B, 0, H, Dh, dt);
   if (st != RAT_OK) return st;
   if (W < 0) return fail(RAT_ERR_INVALID_ARG, "W must be >= 0 (got %d)", W);
@@ -531,6 +542,7 @@ rat_status_t rat_decode_step(const void* q, const void* k, const void* v, const 
   p.B = B; p.H = H; p.Dh = Dh; p.W = W;
   p.bf16 = dt == RAT_BF16;
   p.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)Dh);
+  p.reset_every = reset_every;
   int32_t max_split;
   decode_splits(B, H, dilation, W, max_pos, p.heads.nsplit, max_split);
   p.max_split = max_split;
@@ -560,6 +572,16 @@ rat_status_t rat_decode_step(const void* q, const void* k, const void* v, const 
   hipError_t e = rat::launch_decode(p, stream);
   if (e != hipSuccess) return fail(RAT_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+rat_status_t rat_decode_step(const void* q, const void* k, const void* v, const float* zk,
+                             const float* zv, float* state_k, float* state_v, void* grid_k,
+                             void* grid_v, const int64_t* grid_off, const int32_t* grid_cap,
+                             void* ring_k, void* ring_v, const int32_t* pos, int64_t max_pos,
+                             void* out, int32_t B, int32_t H, int32_t Dh, const int32_t* dilation,
+                             int32_t W, float scale, rat_dtype_t dt, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {  return decode_step_impl(q, k, v, zk, zv, state_k, state_v, grid_k, grid_v, grid_off, grid_cap, ring_k, ring_v,
+                          pos, max_pos, out, B, H, Dh, dilation, W, scale, dt, ws, ws_bytes, stream, 0);
 }
 
 }  // extern "C"
@@ -718,6 +740,55 @@ rat_status_t rat_topk_decode_step(const void* q, const void* k, const void* v, c
   e = rat::launch_topk_attend(tp, stream);
   if (e != hipSuccess) return fail(RAT_ERR_HIP, "top-k attention launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+// ---------------------------------------------------------------------------
+// RAT chunk-local variant: restart every L positions, D = L, W = 1
+// ---------------------------------------------------------------------------
+static bool local_dilation(int32_t H, int32_t L, int32_t* dil) {
+  if (H < 1 || H > RAT_MAX_HEADS || L < 1) return false;
+  for (int h = 0; h < H; ++h) dil[h] = L;
+  return true;
+}
+
+size_t rat_local_prefill_chunk_workspace_size(int32_t B, int32_t T, int32_t H, int32_t Dh, int32_t L,
+                                              int64_t p0, rat_dtype_t dt) {
+  int32_t dil[RAT_MAX_HEADS];
+  if (!local_dilation(H, L, dil)) return 0;
+  return rat_prefill_chunk_workspace_size(B, T, H, Dh, dil, 1, p0, dt);
+}
+
+rat_status_t rat_local_prefill_chunk(const void* q, const void* k, const void* v, const float* zk,
+                                     const float* zv, void* out, float* state_k, float* state_v,
+                                     void* grid_k, void* grid_v, const int64_t* grid_off,
+                                     const int32_t* grid_cap, void* ring_k, void* ring_v, int64_t p0,
+                                     int64_t max_pos, int32_t B, int32_t T, int32_t H, int32_t Dh,
+                                     int32_t L, float scale, rat_dtype_t dt, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+  int32_t dil[RAT_MAX_HEADS];
+  if (!local_dilation(H, L, dil))
+    return fail(RAT_ERR_INVALID_ARG, "need 1 <= H <= %d and L >= 1 (got H = %d, L = %d)", RAT_MAX_HEADS, H, L);
+  return prefill_chunk_impl(q, k, v, zk, zv, out, state_k, state_v, grid_k, grid_v, grid_off, grid_cap, ring_k,
+                            ring_v, p0, max_pos, B, T, H, Dh, dil, 1, scale, dt, ws, ws_bytes, stream, L);
+}
+
+size_t rat_local_decode_workspace_size(int32_t B, int32_t H, int32_t Dh, int32_t L, int64_t max_pos) {
+  int32_t dil[RAT_MAX_HEADS];
+  if (!local_dilation(H, L, dil)) return 0;
+  return rat_decode_workspace_size(B, H, Dh, dil, 1, max_pos);
+}
+
+rat_status_t rat_local_decode_step(const void* q, const void* k, const void* v, const float* zk,
+                                   const float* zv, float* state_k, float* state_v, void* grid_k,
+                                   void* grid_v, const int64_t* grid_off, const int32_t* grid_cap,
+                                   void* ring_k, void* ring_v, const int32_t* pos, int64_t max_pos,
+                                   void* out, int32_t B, int32_t H, int32_t Dh, int32_t L, float scale,
+                                   rat_dtype_t dt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int32_t dil[RAT_MAX_HEADS];
+  if (!local_dilation(H, L, dil))
+    return fail(RAT_ERR_INVALID_ARG, "need 1 <= H <= %d and L >= 1 (got H = %d, L = %d)", RAT_MAX_HEADS, H, L);
+  return decode_step_impl(q, k, v, zk, zv, state_k, state_v, grid_k, grid_v, grid_off, grid_cap, ring_k, ring_v,
+                          pos, max_pos, out, B, H, Dh, dil, 1, scale, dt, ws, ws_bytes, stream, L);
 }
 
 }  // extern "C"

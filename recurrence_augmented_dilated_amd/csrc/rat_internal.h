@@ -130,6 +130,7 @@ struct ScanPlan {
   int64_t arows;       // rows of a kAllToken buffer (>= all_row0 + T)
   int W;               // ring length (ring outputs only)
   int64_t ring_from;   // first absolute position written to the ring
+  int reset_every;     // > 0: chunk-local recurrence, restarted from zero at multiples of it
   int bf16;            // 1: x and outputs are bf16; 0: fp32
   HeadTable heads;
   void* ws;            // workspace base (header + look-back arrays)
@@ -212,6 +213,7 @@ struct DecodePlan {
   float* partials;                               // [B*H*maxsplit][Dh+2]
   int max_split;
   uint32_t* hdr;
+  int reset_every;                               // > 0: state restarts from zero at multiples of it
 };
 hipError_t launch_decode(const DecodePlan& p, hipStream_t s);
 

@@ -109,6 +109,7 @@ struct ScanArgs {
   int64_t arows;      // rows of kAllToken outputs
   int W;              // ring length
   int64_t ring_from;  // first absolute position stored in the ring
+  int reset_every;    // > 0: the state restarts from zero at positions j with j % reset_every == 0
   int n_slabs;        // ntensors * B * slabs_per_bt
   int slabs_per_bt;   // C / (64 * NC)
   uint64_t* agg_a;
@@ -141,14 +142,15 @@ __global__ void scan_prologue(uint32_t* hdr) {
 // Aggregate (prod g, state from a zero carry) of chunk j for one channel,
 // computed straight from the inputs: the look-back's fallback.
 template <typename XT>
-__device__ void chunk_aggregate(const XT* x, const float* z, int64_t C, int T, int j, float& A,
-                                float& Bv) {
+__device__ void chunk_aggregate(const XT* x, const float* z, int64_t C, int T, int j, int64_t p0, int reset,
+                                float& A, float& Bv) {
   A = 1.f;
   Bv = 0.f;
   const int t_end = min(T, (j + 1) * kChunkT);
   for (int t = j * kChunkT; t < t_end; ++t) {
     float g, c;
     gate_pair(z[(int64_t)t * C], g, c);
+    if (reset > 0 && (p0 + t) % reset == 0) g = 0.f;   // restart: the carried state is dropped
     const float xv = sizeof(XT) == 2 ? bf16_to_f32(reinterpret_cast<const bf16_t*>(x)[(int64_t)t * C])
                                      : reinterpret_cast<const float*>(x)[(int64_t)t * C];
     Bv = g * Bv + c * xv;
@@ -210,18 +212,29 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
     }
   }
 
+  // first restart position >= p0 + t0 (chunk-local recurrence), or none
+  int64_t first_reset = INT64_MAX;
+  if (a.reset_every > 0) {
+    const int64_t ja = a.p0 + t0;
+    first_reset = (ja + a.reset_every - 1) / a.reset_every * a.reset_every;
+  }
+
   // ---- pass 1: aggregate of the wave's steps (identity past the end)
   {
     float hl[NC], pp[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) { hl[c] = 0.f; pp[c] = 1.f; }
+    int64_t next_reset = first_reset;
 #pragma unroll
     for (int s = 0; s < kLW; ++s) {
       const bool live = (t0 + s) < T;
+      const bool rs = a.p0 + t0 + s == next_reset;
+      if (rs) next_reset += a.reset_every;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         float g, cc;
         gate_pair(Z::get(zr[s], c), g, cc);
+        if (rs) g = 0.f;
         if (!live) { g = 1.f; cc = 0.f; }
         hl[c] = g * hl[c] + cc * V::get(xr[s], c);
         pp[c] *= g;
@@ -295,7 +308,7 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
           const int chg = cs * SC + cl;
           float Aj, Bj;
           chunk_aggregate<XT>(static_cast<const XT*>(tn.x) + (int64_t)b * T * C + chg,
-                              tn.z + (int64_t)b * T * C + chg, C, T, j, Aj, Bj);
+                              tn.z + (int64_t)b * T * C + chg, C, T, j, a.p0, a.reset_every, Aj, Bj);
           accB = accA * Bj + accB;
           accA *= Aj;
           if (j == 0) {
@@ -344,15 +357,19 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
   const int64_t col_grid_row = col_grid ? grid_row_offset(a.heads, a.B, b, h, 0, a.Dh) +
                                               (int64_t)d * a.heads.gcap[h] : 0;
   float run[NC][4];
+  int64_t next_reset = first_reset;
 
 #pragma unroll
   for (int s = 0; s < kLW; ++s) {
     const int t = t0 + s;
+    const bool rs = a.p0 + t == next_reset;
+    if (rs) next_reset += a.reset_every;
     if (t < T) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         float g, cc;
         gate_pair(Z::get(zr[s], c), g, cc);
+        if (rs) g = 0.f;   // chunk start: the state restarts from zero
         hv[c] = g * hv[c] + cc * V::get(xr[s], c);
       }
       if (tok_all) V::store(out_all + ((int64_t)b * a.arows + a.all_row0 + t) * C + cs * SC + lo, hv);
@@ -471,6 +488,7 @@ hipError_t launch_scan(const ScanPlan& p, hipStream_t s) {
   a.arows = p.arows > 0 ? p.arows : p.T;
   a.W = p.W;
   a.ring_from = p.ring_from;
+  a.reset_every = p.reset_every;
   a.heads = p.heads;
   a.fallback_spins = p.fallback_spins >= 0 ? uint32_t(p.fallback_spins) : kFallbackSpins;
   const int nc = pick_nc(a.C);

@@ -175,3 +175,30 @@ def test_topk_validation():
     assert dec() == -3
     assert L.rat_topk_decode_workspace_size() == 256
     assert R.lib().rat_topk_prefill_workspace_size(1, 4096, 16, 128) > 256
+
+
+def test_local_validation():
+    L = R.lib()
+    H = 2
+    off = (ctypes.c_int64 * H)(0, 16)
+    cap = (ctypes.c_int32 * H)(16, 16)
+
+    def pre(Lc=16, p0=0, T=128, wsb=0, H=H):
+        return L.rat_local_prefill_chunk(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, off, cap, FAKE,
+                                         FAKE, p0, 256, 1, T, H, 128, Lc, -1.0, 1, FAKE, wsb, None)
+
+    assert pre(Lc=0) == -1
+    assert pre(H=0) == -1
+    assert pre(p0=32) == -2                  # chunk start must be a multiple of 64
+    assert pre() == -3
+    assert L.rat_local_prefill_chunk_workspace_size(1, 128, 2, 128, 16, 0, 1) > 0
+    assert L.rat_local_prefill_chunk_workspace_size(1, 128, 2, 128, 0, 0, 1) == 0
+
+    def dec(Lc=16, wsb=0, pos=FAKE):
+        return L.rat_local_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, off, cap, FAKE, FAKE,
+                                       pos, 256, FAKE, 1, H, 128, Lc, -1.0, 1, FAKE, wsb, None)
+
+    assert dec(Lc=0) == -1
+    assert dec(pos=None) == -1
+    assert dec() == -3
+    assert L.rat_local_decode_workspace_size(1, H, 128, 16, 256) > 256
