@@ -34,6 +34,12 @@ CONFIGS = {
             dtype="bf16"),
     5: dict(kind="decode", B=128, H=32, Dh=128, ctx=131072, D=[1] * 8 + [16] * 12 + [64] * 12, W=64,
             steps=1024, mu=2.0, dtype="bf16"),
+    # auxiliary workloads of the operator's other forms (not the headline line)
+    6: dict(kind="chunked", B=1, H=16, Dh=128, T=16384, D=16, W=128, chunk=4096, dtype="bf16", mu=2.0),
+    7: dict(kind="topk_decode", B=128, H=16, Dh=128, ctx=32768, block=64, topk=16, score=0, steps=256,
+            dtype="bf16", mu=2.0),
+    8: dict(kind="topk_prefill", B=1, H=16, Dh=128, T=4096, block=64, topk=16, score=1, dtype="bf16", mu=2.0),
+    9: dict(kind="local", B=1, H=16, Dh=128, T=16384, L=16, dtype="bf16", mu=2.0),
 }
 
 
@@ -223,6 +229,209 @@ def bench_decode(c, steps, warmup, torch, R, inputs):
 
 
 # ---------------------------------------------------------------------------
+# auxiliary workloads: chunked prefill, top-k block attention, chunk-local
+# ---------------------------------------------------------------------------
+
+def bench_chunked(c, steps, warmup, torch, R, inputs):
+    """Config-2 sequence prefilled in chunks into a decode cache (handoff)."""
+    dev = "cuda:0"
+    B, H, Dh, T, D, W, ch = c["B"], c["H"], c["Dh"], c["T"], c["D"], c["W"], c["chunk"]
+    x = inputs.prefill_inputs(B, T, H, Dh, dtype=torch.bfloat16, mu=c["mu"], seed=2, device=dev)
+    max_pos = T + 1024
+    off, cap, rows = R.rat_grid_layout(H, [D] * H, max_pos)
+    gk = torch.zeros(B * rows * Dh, dtype=torch.bfloat16, device=dev)
+    gv = torch.zeros_like(gk)
+    rk = torch.zeros((B, H, W, Dh), dtype=torch.bfloat16, device=dev)
+    rv = torch.zeros_like(rk)
+    sk = torch.zeros((B, H, Dh), dtype=torch.float32, device=dev)
+    sv = torch.zeros_like(sk)
+    parts = [{n: t[:, p0:p0 + ch].contiguous() for n, t in x.items()} for p0 in range(0, T, ch)]
+    out = torch.empty((B, ch, H, Dh), dtype=torch.bfloat16, device=dev)
+    ws = torch.zeros(max(R.rat_prefill_chunk_workspace_size(B, ch, H, Dh, [D] * H, W, p0) for p0 in range(0, T, ch)),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        sk.zero_()
+        sv.zero_()
+        for i, d in enumerate(parts):
+            R.rat_prefill_chunk(d["q"], d["k"], d["v"], d["zk"], d["zv"], sk, sv, gk, gv, off, cap, rk, rv, i * ch,
+                                max_pos, [D] * H, W, out=out, ws=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ms = time_loop(step, steps, torch)
+    log(f"[bench] chunked prefill ({T // ch} chunks of {ch}) {ms:.3f} ms/sequence")
+    return ms
+
+
+def topk_decode_bytes(c, t):
+    """Algorithmic HBM bytes of one top-k decode step at position t."""
+    B, H, Dh, blk, k = c["B"], c["H"], c["Dh"], c["block"], c["topk"]
+    local = t // blk
+    ncand = max(0, local - 1)
+    nstats = 2 if c["score"] == 0 else 1                  # Quest reads min and max, MoBA the mean
+    kept = min(k, ncand) * blk + (blk if local > 0 else 0) + (t - local * blk + 1)
+    per = (3 * Dh * 2 + 2 * Dh * 4          # q, k, v, zk, zv
+           + 2 * 2 * Dh * 4                 # fp32 states read and written
+           + 2 * Dh * 2                     # the new cache rows
+           + ncand * nstats * Dh * 4        # summaries of the candidate blocks
+           + kept * Dh * 2 * 2              # key and value rows of the kept blocks
+           + Dh * 2)                        # output
+    if (t + 1) % blk == 0:
+        per += blk * Dh * 2 + 3 * Dh * 4    # summary of the completed block
+    return B * H * per
+
+
+def bench_topk_decode(c, steps, warmup, torch, R):
+    dev = "cuda:0"
+    B, H, Dh, blk, k, ctx = c["B"], c["H"], c["Dh"], c["block"], c["topk"], c["ctx"]
+    max_pos = ctx + max(steps, warmup) + blk
+    max_pos = (max_pos + blk - 1) // blk * blk
+    cache = R.topk_cache(B, H, Dh, max_pos, blk, torch.bfloat16, dev)
+    g = torch.Generator(device=dev).manual_seed(7)
+    for name in ("cache_k", "cache_v"):
+        buf = cache[name]
+        for h in range(H):
+            buf[h].copy_(torch.randn(buf[h].shape, generator=g, device=dev).to(torch.bfloat16))
+    cache["state_k"].normal_(generator=g)
+    cache["state_v"].normal_(generator=g)
+    R.rat_topk_summarize(cache, 0, ctx // blk, max_pos, blk)
+    from recurrence_augmented_dilated_amd import inputs
+    n_in = max(steps, warmup)
+    st = inputs.decode_step_inputs(B, H, Dh, n_in, mu=c["mu"], seed=5, device=dev)
+    pos = torch.full((B,), ctx, dtype=torch.int32, device=dev)
+    out = torch.empty((B, H, Dh), dtype=torch.bfloat16, device=dev)
+    ws = torch.zeros(R.lib().rat_topk_decode_workspace_size(), dtype=torch.uint8, device=dev)
+
+    def run(n):
+        for i in range(n):
+            R.rat_topk_decode_step(st["q"][i], st["k"][i], st["v"][i], st["zk"][i], st["zv"][i], cache, pos, max_pos,
+                                   blk, k, c["score"], out=out, ws=ws)
+            pos.add_(1)
+
+    run(warmup)
+    torch.cuda.synchronize()
+    pos.fill_(ctx)
+    ms = time_loop(lambda: run(1), steps, torch)
+    err = R.workspace_error(ws)
+    nbytes = sum(topk_decode_bytes(c, ctx + i) for i in range(steps)) / steps
+    log(f"[bench] top-k decode {ms:.3f} ms/step, {nbytes / (ms * 1e-3) / 1e9:.0f} GB/s, ws error {err}")
+    return ms, nbytes, err
+
+
+def topk_prefill_flops(c):
+    """fp32 VALU flops of top-k block prefill attention: scoring every
+    candidate block and the softmax attention over the kept positions."""
+    B, H, Dh, T, blk, k = c["B"], c["H"], c["Dh"], c["T"], c["block"], c["topk"]
+    total = 0
+    for t in range(T):
+        local = t // blk
+        ncand = max(0, local - 1)
+        kept = min(k, ncand) * blk + (blk if local > 0 else 0) + (t - local * blk + 1)
+        total += (2 * Dh if c["score"] == 1 else 3 * Dh) * ncand + 4 * Dh * kept
+    return B * H * total
+
+
+def bench_topk_prefill(c, steps, warmup, torch, R, inputs):
+    dev = "cuda:0"
+    B, H, Dh, T, blk, k = c["B"], c["H"], c["Dh"], c["T"], c["block"], c["topk"]
+    x = inputs.prefill_inputs(B, T, H, Dh, dtype=torch.bfloat16, mu=c["mu"], seed=2, device=dev)
+    max_pos = (T + blk - 1) // blk * blk
+    cache = R.topk_cache(B, H, Dh, max_pos, blk, torch.bfloat16, dev)
+    out = torch.empty_like(x["q"])
+    ws = torch.zeros(R.lib().rat_topk_prefill_workspace_size(B, T, H, Dh), dtype=torch.uint8, device=dev)
+
+    def step():
+        cache["state_k"].zero_()
+        cache["state_v"].zero_()
+        R.rat_topk_prefill(x["q"], x["k"], x["v"], x["zk"], x["zv"], cache, 0, max_pos, blk, k, c["score"], out=out,
+                           ws=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ms = time_loop(step, steps, torch)
+    log(f"[bench] top-k prefill {ms:.3f} ms/step")
+    return ms
+
+
+def bench_local(c, steps, warmup, torch, R, inputs):
+    dev = "cuda:0"
+    B, H, Dh, T, L = c["B"], c["H"], c["Dh"], c["T"], c["L"]
+    x = inputs.prefill_inputs(B, T, H, Dh, dtype=torch.bfloat16, mu=c["mu"], seed=2, device=dev)
+    max_pos = T + 64
+    off, cap, rows = R.rat_grid_layout(H, [L] * H, max_pos)
+    gk = torch.zeros(B * rows * Dh, dtype=torch.bfloat16, device=dev)
+    gv = torch.zeros_like(gk)
+    rk = torch.zeros((B, H, 1, Dh), dtype=torch.bfloat16, device=dev)
+    rv = torch.zeros_like(rk)
+    sk = torch.zeros((B, H, Dh), dtype=torch.float32, device=dev)
+    sv = torch.zeros_like(sk)
+    out = torch.empty_like(x["q"])
+
+    def step():
+        R.rat_local_prefill_chunk(x["q"], x["k"], x["v"], x["zk"], x["zv"], sk, sv, gk, gv, off, cap, rk, rv, 0,
+                                  max_pos, L, out=out)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ms = time_loop(step, steps, torch)
+    log(f"[bench] chunk-local prefill (L={L}) {ms:.3f} ms/step")
+    return ms
+
+
+def aux_result(cfg_id, c, a, torch, R, inputs):
+    """One JSON result for an auxiliary workload (configs 6-9)."""
+    res = {"unit": "tokens/s", "n_gpus": 1, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "data": "synthetic", "dtype": c["dtype"], "steps": a.steps, "warmup": a.warmup}
+    kind = c["kind"]
+    if kind in ("chunked", "local"):
+        if kind == "chunked":
+            ms = bench_chunked(c, a.steps, a.warmup, torch, R, inputs)
+            w = prefill_work(c)
+            wl = (f"chunked prefill B={c['B']} H={c['H']} Dh={c['Dh']} T={c['T']} in chunks of {c['chunk']} "
+                  f"D={c['D']} W={c['W']} bf16 into a decode cache")
+            metric = "chunked prefill tokens/s (prefill continuing a decode cache)"
+        else:
+            ms = bench_local(c, a.steps, a.warmup, torch, R, inputs)
+            w = prefill_work(dict(c, D=c["L"], W=1))
+            wl = f"RAT chunk-local prefill B={c['B']} H={c['H']} Dh={c['Dh']} T={c['T']} L={c['L']} bf16"
+            metric = "chunk-local (RAT) prefill tokens/s"
+        tfs = w["attn_flops"] / (ms * 1e-3)
+        res.update(metric=metric, value=c["B"] * c["T"] / (ms * 1e-3), ms_per_step=ms,
+                   config={"workload": wl, "config_id": cfg_id},
+                   roofline={"kernel": "whole step (recurrence + attention)", "bound": "mfma",
+                             "achieved": tfs / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                             "frac": tfs / PEAK_BF16, "traffic": None,
+                             "note": "attention flops over the whole step time"})
+    elif kind == "topk_decode":
+        ms, nbytes, err = bench_topk_decode(c, a.steps, a.warmup, torch, R)
+        gbs = nbytes / (ms * 1e-3)
+        res.update(metric="top-k block attention decode tokens/s", value=c["B"] / (ms * 1e-3), ms_per_step=ms,
+                   config={"workload": f"top-k decode B={c['B']} H={c['H']} Dh={c['Dh']} ctx={c['ctx']} "
+                                       f"block={c['block']} topk={c['topk']} {'quest' if c['score'] == 0 else 'moba'}",
+                           "config_id": cfg_id},
+                   roofline={"kernel": "whole step (append + select + attend)", "bound": "hbm",
+                             "achieved": gbs / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": gbs / PEAK_HBM,
+                             "traffic": None},
+                   ws_error=err)
+    elif kind == "topk_prefill":
+        ms = bench_topk_prefill(c, a.steps, a.warmup, torch, R, inputs)
+        fl = topk_prefill_flops(c)
+        res.update(metric="top-k block attention prefill tokens/s", value=c["B"] * c["T"] / (ms * 1e-3),
+                   ms_per_step=ms,
+                   config={"workload": f"top-k prefill B={c['B']} H={c['H']} Dh={c['Dh']} T={c['T']} "
+                                       f"block={c['block']} topk={c['topk']} {'quest' if c['score'] == 0 else 'moba'}",
+                           "config_id": cfg_id},
+                   roofline={"kernel": "whole step (recurrence + summaries + select + attend)", "bound": "alu",
+                             "achieved": fl / (ms * 1e-3) / 1e12, "peak": PEAK_F32_VALU / 1e12, "unit": "TFLOP/s",
+                             "frac": fl / (ms * 1e-3) / PEAK_F32_VALU, "traffic": None})
+    return res
+
+
+# ---------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle as it stands, one thread
 # ---------------------------------------------------------------------------
 
@@ -400,6 +609,9 @@ def main():
 
     cfg_id = a.config or 2
     c = CONFIGS[cfg_id]
+    if c["kind"] not in ("prefill", "decode"):
+        print(json.dumps(aux_result(cfg_id, c, a, torch, R, inputs)), flush=True)
+        return
     result = {"metric": "prefill & decode tokens/s of RAT+ dilated op; % HBM/MFMA roofline",
               "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True, "scaling": "weak",
               "vs_baseline": None, "data": "synthetic"}

@@ -300,6 +300,13 @@ rat_status_t rat_topk_prefill(const void* q, const void* k, const void* v, const
                               float scale, rat_dtype_t dtype, void* ws, size_t ws_bytes,
                               hipStream_t stream);
 
+/* Summaries (min, max, mean of the key states) of blocks j_lo .. j_hi-1 of
+ * every (h, b) from cache_k, e.g. for a cache filled by other means;
+ * 0 <= j_lo <= j_hi <= max_pos / block. */
+rat_status_t rat_topk_summarize(const void* cache_k, float* summary, int64_t j_lo, int64_t j_hi,
+                                int64_t max_pos, int32_t B, int32_t H, int32_t Dh, int32_t block,
+                                rat_dtype_t dtype, hipStream_t stream);
+
 /* One new token per sequence at position pos[b] (device int32 [B], every
  * entry in [0, max_pos), others: error bit 1 and a zero output): state
  * update, cache row pos[b], the summary of a block that row completes, then

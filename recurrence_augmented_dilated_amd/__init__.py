@@ -104,6 +104,8 @@ def lib():
             L.rat_local_decode_step.restype = c_int
             L.rat_local_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, c_i64, vp,
                                                 c_int, c_int, c_int, c_int, c_f, c_int, vp, c_sz, vp]
+            L.rat_topk_summarize.restype = c_int
+            L.rat_topk_summarize.argtypes = [vp, vp, c_i64, c_i64, c_i64, c_int, c_int, c_int, c_int, c_int, vp]
             _lib = L
     return _lib
 
@@ -393,6 +395,14 @@ def rat_topk_prefill(q, k, v, zk, zv, cache, p0, max_pos, block, topk, score=TOP
         int(max_pos), B, T, H, Dh, int(block), int(topk), int(score), s, _dtype_code(q), _ptr(ws), ws.numel(),
         _stream(q.device)))
     return out
+
+
+def rat_topk_summarize(cache, j_lo, j_hi, max_pos, block):
+    """Block summaries j_lo .. j_hi-1 of cache["cache_k"] into cache["summary"]."""
+    H, B, _, Dh = cache["cache_k"].shape
+    _check(lib().rat_topk_summarize(_ptr(cache["cache_k"]), _ptr(cache["summary"]), int(j_lo), int(j_hi),
+                                    int(max_pos), B, H, Dh, int(block), _dtype_code(cache["cache_k"]),
+                                    _stream(cache["cache_k"].device)))
 
 
 def rat_topk_decode_step(q, k, v, zk, zv, cache, pos, max_pos, block, topk, score=TOPK_QUEST, scale=None,

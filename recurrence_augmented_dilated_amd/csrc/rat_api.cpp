@@ -693,6 +693,29 @@ rat_status_t rat_topk_prefill(const void* q, const void* k, const void* v, const
   return ok();
 }
 
+rat_status_t rat_topk_summarize(const void* cache_k, float* summary, int64_t j_lo, int64_t j_hi,
+                                int64_t max_pos, int32_t B, int32_t H, int32_t Dh, int32_t block,
+                                rat_dtype_t dt, hipStream_t stream) {
+  rat_status_t st = check_common(B, 0, H, Dh, dt);
+  if (st != RAT_OK) return st;
+  if ((st = check_topk(block, 0, RAT_TOPK_QUEST, max_pos)) != RAT_OK) return st;
+  if (j_lo < 0 || j_hi < j_lo || j_hi > max_pos / block)
+    return fail(RAT_ERR_INVALID_ARG, "need 0 <= j_lo <= j_hi <= max_pos / block (got %lld, %lld)",
+                (long long)j_lo, (long long)j_hi);
+  if (j_hi == j_lo) return ok();
+  if ((st = check_ptr(cache_k, "cache_k", false)) != RAT_OK) return st;
+  if ((st = check_ptr(summary, "summary", false)) != RAT_OK) return st;
+  rat::TopkPlan tp;
+  std::memset(&tp, 0, sizeof(tp));
+  tp.cache_k = cache_k; tp.summary = summary;
+  tp.max_pos = max_pos;
+  tp.B = B; tp.H = H; tp.Dh = Dh; tp.block = block;
+  tp.bf16 = dt == RAT_BF16;
+  hipError_t e = rat::launch_topk_stats(tp, j_lo, j_hi, stream);
+  if (e != hipSuccess) return fail(RAT_ERR_HIP, "block summary launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 size_t rat_topk_decode_workspace_size(void) { return sizeof(rat::WsHeader); }
 
 rat_status_t rat_topk_decode_step(const void* q, const void* k, const void* v, const float* zk,

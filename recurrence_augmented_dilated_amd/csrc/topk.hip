@@ -14,7 +14,7 @@
 // Every recurrent state sits in a cache [H][B][max_pos][Dh]; the summaries
 // of complete blocks in fp32 [H][B][max_pos / block][3][Dh].  One workgroup
 // handles one query: it scores the candidate blocks from the summaries into
-// LDS, takes the top k by repeated block-wide argmax, then streams the rows
+// LDS, takes the top k by repeated wave-wide argmax, then streams the rows
 // of the kept blocks (Dh / 8 lanes per row, online softmax per lane group,
 // waves merged in LDS).
 #include "rat_internal.h"
@@ -24,7 +24,7 @@ namespace rat {
 namespace {
 
 constexpr int kAW = 4;        // waves per attend workgroup
-constexpr int kAUnroll = 4;
+constexpr int kAUnroll = 8;   // row steps in flight per wave
 
 template <typename ET> __device__ __forceinline__ float ld1(const ET* p);
 template <> __device__ __forceinline__ float ld1<bf16_t>(const bf16_t* p) { return bf16_to_f32(*p); }
@@ -126,10 +126,8 @@ __global__ __launch_bounds__(kAW * 64) void topk_attend_kernel(const TopkPlan p)
   constexpr int LPK = DH / 8;      // lanes per row
   constexpr int KPW = 64 / LPK;    // rows per wave step
   __shared__ float s_q[DH];
-  __shared__ float s_sc[kTopkMaxBlocks];
+  extern __shared__ float s_sc[];     // candidate scores: max_pos / block floats (launch-time size)
   __shared__ int s_list[kTopkMaxK + 2];
-  __shared__ float s_bv[kAW];
-  __shared__ int s_bi[kAW];
   __shared__ float s_m[kAW], s_l[kAW];
   __shared__ float s_acc[kAW][DH];
 
@@ -170,30 +168,48 @@ __global__ __launch_bounds__(kAW * 64) void topk_attend_kernel(const TopkPlan p)
   const int64_t nbcap = p.max_pos / p.block;
   const float* sb = p.summary + summary_off(p.B, nbcap, h, b, 0, DH);
 
-  // ---- scores of the candidates (score of block j + 1 in s_sc[j])
-  for (int j = tid; j < ncand; j += kAW * 64) {
-    const float* st = sb + (int64_t)(j + 1) * 3 * DH;
-    float s = 0.f;
-    if (p.score == kTopkQuest) {
-#pragma unroll 8
-      for (int d = 0; d < DH; ++d) s += fmaxf(s_q[d] * st[d], s_q[d] * st[DH + d]);
-    } else {
-#pragma unroll 8
-      for (int d = 0; d < DH; ++d) s = fmaf(s_q[d], st[2 * DH + d], s);
+  // ---- scores of the candidates (score of block j + 1 in s_sc[j]): LPK
+  // lanes per candidate, eight head dims per lane, 16-byte loads
+  {
+    float qd[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qd[i] = s_q[8 * c + i];
+    const int slot = wave * KPW + rg;                 // candidate slot of this lane group
+    for (int j0 = 0; j0 < ncand; j0 += kAW * KPW) {
+      const int j = j0 + slot;
+      const bool ok = j < ncand;
+      const float* st = sb + (int64_t)(ok ? j + 1 : 0) * 3 * DH + 8 * c;
+      float part = 0.f;
+      if (p.score == kTopkQuest) {
+        const float4 a0 = reinterpret_cast<const float4*>(st)[0], a1 = reinterpret_cast<const float4*>(st)[1];
+        const float4 b0 = reinterpret_cast<const float4*>(st + DH)[0], b1 = reinterpret_cast<const float4*>(st + DH)[1];
+        const float mn[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const float mx[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part += fmaxf(qd[i] * mn[i], qd[i] * mx[i]);
+      } else {
+        const float4 a0 = reinterpret_cast<const float4*>(st + 2 * DH)[0];
+        const float4 a1 = reinterpret_cast<const float4*>(st + 2 * DH)[1];
+        const float me[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part = fmaf(qd[i], me[i], part);
+      }
+      const float sc = group_sum<LPK>(part);
+      if (ok && c == 0) s_sc[j] = sc == sc ? sc : -INFINITY;   // NaN marks "taken" below
     }
-    s_sc[j] = s == s ? s : -INFINITY;   // NaN marks "taken" below
   }
   __syncthreads();
 
-  // ---- the top k (or all candidates when there are at most k)
+  // ---- the top k (or all candidates when there are at most k), taken by
+  // one wave: per round a wave-wide argmax, no workgroup barrier
   const int nsel = ncand < p.topk ? ncand : p.topk;
   if (ncand <= p.topk) {
     for (int j = tid; j < ncand; j += kAW * 64) s_list[1 + j] = j + 1;
-  } else {
+  } else if (wave == 0) {
     for (int r = 0; r < nsel; ++r) {
       float bv = -INFINITY;
       int bi = 0x7fffffff;
-      for (int j = tid; j < ncand; j += kAW * 64) {
+      for (int j = lane; j < ncand; j += 64) {
         const float v = s_sc[j];
         if (better(v, j, bv, bi)) { bv = v; bi = j; }
       }
@@ -203,19 +219,14 @@ __global__ __launch_bounds__(kAW * 64) void topk_attend_kernel(const TopkPlan p)
         const int oi = __shfl_xor(bi, off);
         if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
       }
-      if (lane == 0) { s_bv[wave] = bv; s_bi[wave] = bi; }
-      __syncthreads();
-      if (tid == 0) {
-        float fv = s_bv[0];
-        int fi = s_bi[0];
-        for (int w = 1; w < kAW; ++w)
-          if (better(s_bv[w], s_bi[w], fv, fi)) { fv = s_bv[w]; fi = s_bi[w]; }
-        s_list[1 + r] = fi + 1;
-        s_sc[fi] = __builtin_nanf("");
+      // every lane holds the winner; one lane marks it taken (the wave's
+      // later LDS reads are ordered after this write)
+      if (lane == 0) {
+        s_list[1 + r] = bi + 1;
+        s_sc[bi] = __builtin_nanf("");
       }
-      __syncthreads();
     }
-    if (tid == 0) {   // ascending block order
+    if (lane == 0) {   // ascending block order
       for (int i = 2; i <= nsel; ++i) {
         const int x = s_list[i];
         int k = i - 1;
@@ -336,12 +347,14 @@ hipError_t launch_topk_attend(const TopkPlan& p, hipStream_t s) {
   const int64_t blocks = p.pos ? (int64_t)p.B * p.H : (int64_t)p.B * p.T * p.H;
   if (blocks <= 0) return hipSuccess;
   const dim3 grid((unsigned)blocks), threads(kAW * 64);
+  // candidate scores in dynamic LDS: at most max_pos / block of them
+  const size_t lds = sizeof(float) * (size_t)(p.max_pos / p.block > 0 ? p.max_pos / p.block : 1);
   if (p.bf16) {
-    if (p.Dh == 128) hipLaunchKernelGGL((topk_attend_kernel<bf16_t, 128>), grid, threads, 0, s, p);
-    else hipLaunchKernelGGL((topk_attend_kernel<bf16_t, 64>), grid, threads, 0, s, p);
+    if (p.Dh == 128) hipLaunchKernelGGL((topk_attend_kernel<bf16_t, 128>), grid, threads, lds, s, p);
+    else hipLaunchKernelGGL((topk_attend_kernel<bf16_t, 64>), grid, threads, lds, s, p);
   } else {
-    if (p.Dh == 128) hipLaunchKernelGGL((topk_attend_kernel<float, 128>), grid, threads, 0, s, p);
-    else hipLaunchKernelGGL((topk_attend_kernel<float, 64>), grid, threads, 0, s, p);
+    if (p.Dh == 128) hipLaunchKernelGGL((topk_attend_kernel<float, 128>), grid, threads, lds, s, p);
+    else hipLaunchKernelGGL((topk_attend_kernel<float, 64>), grid, threads, lds, s, p);
   }
   return hipGetLastError();
 }

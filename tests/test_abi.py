@@ -202,3 +202,11 @@ def test_local_validation():
     assert dec(pos=None) == -1
     assert dec() == -3
     assert L.rat_local_decode_workspace_size(1, H, 128, 16, 256) > 256
+
+
+def test_topk_summarize_validation():
+    L = R.lib()
+    assert L.rat_topk_summarize(FAKE, FAKE, 0, 17, 1024, 1, 2, 128, 64, 1, None) == -1   # j_hi > max_pos / block
+    assert L.rat_topk_summarize(FAKE, FAKE, 5, 4, 1024, 1, 2, 128, 64, 1, None) == -1
+    assert L.rat_topk_summarize(None, FAKE, 0, 4, 1024, 1, 2, 128, 64, 1, None) == -1
+    assert L.rat_topk_summarize(None, None, 3, 3, 1024, 1, 2, 128, 64, 1, None) == 0      # empty range: no-op

@@ -167,3 +167,22 @@ def test_topk_decode_bad_position():
     assert torch.all(out[1] == 0)
     assert torch.all(cache["cache_k"][:, 1] == 0)     # the bad sequence's cache is untouched
     assert torch.any(cache["cache_k"][:, 0, 5] != 0)
+
+
+def test_topk_summarize_matches_block_statistics():
+    """rat_topk_summarize over a cache filled by other means equals the
+    oracle's block statistics of the same (bf16) values."""
+    R = need_gpu()
+    B, H, Dh, block, max_pos = 2, 3, 128, 32, 512
+    cache = R.topk_cache(B, H, Dh, max_pos, block, torch.bfloat16, DEV)
+    g = torch.Generator(device=DEV).manual_seed(7)
+    cache["cache_k"].copy_(torch.randn(cache["cache_k"].shape, generator=g, device=DEV).to(torch.bfloat16))
+    R.rat_topk_summarize(cache, 2, 12, max_pos, block)
+    torch.cuda.synchronize()
+    ck = f64(cache["cache_k"])                       # [H, B, max_pos, Dh]
+    kmin, kmax, kmean = TK.block_stats(np.transpose(ck, (1, 2, 0, 3)), block)   # [B, nb, H, Dh]
+    s = f64(cache["summary"])                        # [H, B, nb, 3, Dh]
+    for h in range(H):
+        for i, ref in enumerate((kmin, kmax, kmean)):
+            assert np.max(np.abs(s[h, :, 2:12, i] - ref[:, 2:12, h])) <= 1e-5
+        assert np.all(s[h, :, :2] == 0) and np.all(s[h, :, 12:] == 0)   # other blocks untouched
