@@ -50,7 +50,10 @@ def log(msg):
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "recurrence_augmented_dilated_amd", "csrc")
 KERNEL_SOURCES = {"scan": ["scan.hip", "rat_internal.h"], "attention": ["prefill_attn.hip", "rat_internal.h"],
-                  "decode": ["decode.hip", "rat_internal.h"]}
+                  "decode": ["decode.hip", "kv_stream.h", "rat_internal.h"],
+                  "topk_attend": ["topk.hip", "kv_stream.h", "rat_internal.h"],
+                  "topk_stats": ["topk.hip", "rat_internal.h"], "topk_append": ["topk.hip", "rat_internal.h"],
+                  "grid_to_col": ["chunk.hip", "rat_internal.h"], "ring_prefix": ["chunk.hip", "rat_internal.h"]}
 
 
 def source_hash(kernel):
@@ -415,7 +418,7 @@ def aux_result(cfg_id, c, a, torch, R, inputs):
                            "config_id": cfg_id},
                    roofline={"kernel": "whole step (append + select + attend)", "bound": "hbm",
                              "achieved": gbs / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": gbs / PEAK_HBM,
-                             "traffic": None},
+                             "traffic": measured_traffic("topk_attend", f"topk_decode_config{cfg_id}")},
                    ws_error=err)
     elif kind == "topk_prefill":
         ms = bench_topk_prefill(c, a.steps, a.warmup, torch, R, inputs)
@@ -475,7 +478,10 @@ def measure_copy(torch):
 # offline: rocprofv3 CSV output -> short summaries under profiles/ (CPU only)
 # ---------------------------------------------------------------------------
 
-KERNEL_PATTERNS = {"scan": "scan_kernel", "attention": "attn_bf16_kernel", "decode": "decode_kernel"}
+KERNEL_PATTERNS = {"scan": "scan_kernel", "attention": "attn_bf16_kernel", "decode": "decode_kernel",
+                   "topk_attend": "topk_attend_kernel", "topk_stats": "topk_stats_kernel",
+                   "topk_append": "topk_append_kernel", "grid_to_col": "grid_to_col_kernel",
+                   "ring_prefix": "ring_prefix_kernel"}
 COPY_BYTES = 1 << 30   # --calibrate-copy: bytes read and bytes written by one copy
 
 
