@@ -42,6 +42,31 @@ __global__ void ring_prefix_kernel(const RingPrefixPlan p) {
   }
 }
 
+// One thread per (b, h, d, r) for the rows r of positions ring_from + r:
+// ring slot (ring_from + r) % W <- all-state row ring_from - base + r.
+template <typename ET>
+__global__ void states_to_ring_kernel(const RingPrefixPlan p, int64_t ring_from, int64_t n) {
+  const int64_t total = (int64_t)p.B * p.H * n * p.Dh;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int d = int(i % p.Dh);
+  int64_t rest = i / p.Dh;
+  const int64_t r = rest % n;
+  rest /= n;
+  const int h = int(rest % p.H);
+  const int b = int(rest / p.H);
+  const int64_t j = ring_from + r;            // absolute position
+  const int64_t row = j - p.base;             // all-state row
+  const int64_t C = (int64_t)p.H * p.Dh;
+  const ET kv = static_cast<const ET*>(p.all_k)[((int64_t)b * p.arows + row) * C + (int64_t)h * p.Dh + d];
+  const ET vv = p.bf16 ? static_cast<const ET*>(p.all_v)[(((int64_t)b * p.H + h) * p.Dh + d) * p.tpad +
+                                                         col_key_pos(row, d)]
+                       : static_cast<const ET*>(p.all_v)[((int64_t)b * p.arows + row) * C + (int64_t)h * p.Dh + d];
+  const int64_t dst = (((int64_t)b * p.H + h) * p.W + j % p.W) * p.Dh + d;
+  static_cast<ET*>(p.ring_k)[dst] = kv;
+  static_cast<ET*>(p.ring_v)[dst] = vv;
+}
+
 // One thread per (b, h, d, column i < vgcap[h]): column i of row d of the
 // transposed grid values is grid entry i (zero past rows[h]).  Consecutive
 // threads take consecutive columns, so the writes are contiguous.
@@ -79,6 +104,19 @@ hipError_t launch_ring_prefix(const RingPrefixPlan& p, hipStream_t s) {
     hipLaunchKernelGGL(ring_prefix_kernel<bf16_t>, dim3((unsigned)blocks), dim3(threads), 0, s, p);
   else
     hipLaunchKernelGGL(ring_prefix_kernel<float>, dim3((unsigned)blocks), dim3(threads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_states_to_ring(const RingPrefixPlan& p, int64_t ring_from, hipStream_t s) {
+  const int64_t n = p.base + p.arows - ring_from;    // positions ring_from .. base + arows - 1
+  const int64_t total = (int64_t)p.B * p.H * n * p.Dh;
+  if (n <= 0 || total <= 0) return hipSuccess;
+  const int threads = 256;
+  const int64_t blocks = (total + threads - 1) / threads;
+  if (p.bf16)
+    hipLaunchKernelGGL(states_to_ring_kernel<bf16_t>, dim3((unsigned)blocks), dim3(threads), 0, s, p, ring_from, n);
+  else
+    hipLaunchKernelGGL(states_to_ring_kernel<float>, dim3((unsigned)blocks), dim3(threads), 0, s, p, ring_from, n);
   return hipGetLastError();
 }
 

@@ -400,17 +400,14 @@ static rat_status_t prefill_chunk_impl(const void* q, const void* k, const void*
   //    entries and ring slots into the cache, final states
   rat::ScanPlan sp;
   std::memset(&sp, 0, sizeof(sp));
-  sp.ten[0] = {k, zk, h0k, all_k, grid_k, state_k, rat::kAllToken, rat::kGridHeadRow, W > 0 ? ring_k : nullptr};
-  sp.ten[1] = {v, zv, h0v, all_v, grid_v, state_v, bf16 ? rat::kAllHeadCol : rat::kAllToken, rat::kGridHeadRow,
-               W > 0 ? ring_v : nullptr};
+  sp.ten[0] = {k, zk, h0k, all_k, grid_k, state_k, rat::kAllToken, rat::kGridHeadRow};
+  sp.ten[1] = {v, zv, h0v, all_v, grid_v, state_v, bf16 ? rat::kAllHeadCol : rat::kAllToken, rat::kGridHeadRow};
   sp.ntensors = 2;
   sp.B = B; sp.T = T; sp.H = H; sp.Dh = Dh;
   sp.tpad = bf16 ? cv.tpad : cv.arows;
   sp.p0 = p0;
   sp.all_row0 = cv.all_row0;
   sp.arows = cv.arows;
-  sp.W = W;
-  sp.ring_from = std::max<int64_t>(p0, p0 + T - W);
   sp.reset_every = reset_every;
   sp.bf16 = bf16;
   sp.heads = cache;
@@ -418,6 +415,18 @@ static rat_status_t prefill_chunk_impl(const void* q, const void* k, const void*
   sp.fallback_spins = scan_fallback_spins();
   e = rat::launch_scan(sp, stream);
   if (e != hipSuccess) return fail(RAT_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
+  if (W > 0) {   // the chunk's last min(W, T) states into the ring
+    rat::RingPrefixPlan rp;
+    rp.ring_k = ring_k; rp.ring_v = ring_v;
+    rp.all_k = all_k; rp.all_v = all_v;
+    rp.B = B; rp.H = H; rp.Dh = Dh; rp.W = W;
+    rp.base = cv.base; rp.n_pre = cv.all_row0;
+    rp.ring_lo = 0;
+    rp.arows = cv.arows; rp.tpad = cv.tpad;
+    rp.bf16 = bf16;
+    e = rat::launch_states_to_ring(rp, std::max<int64_t>(p0, p0 + T - W), stream);
+    if (e != hipSuccess) return fail(RAT_ERR_HIP, "ring update launch: %s", hipGetErrorString(e));
+  }
 
   // 4. bf16: the grid values the chunk's queries see, transposed
   rat::AttnPlan ap;
@@ -661,8 +670,8 @@ rat_status_t rat_topk_prefill(const void* q, const void* k, const void* v, const
   // recurrence: every state of positions p0 .. p0+T-1 into the caches
   rat::ScanPlan sp;
   std::memset(&sp, 0, sizeof(sp));
-  sp.ten[0] = {k, zk, h0k, nullptr, cache_k, state_k, rat::kAllToken, rat::kGridHeadRow, nullptr};
-  sp.ten[1] = {v, zv, h0v, nullptr, cache_v, state_v, rat::kAllToken, rat::kGridHeadRow, nullptr};
+  sp.ten[0] = {k, zk, h0k, nullptr, cache_k, state_k, rat::kAllToken, rat::kGridHeadRow};
+  sp.ten[1] = {v, zv, h0v, nullptr, cache_v, state_v, rat::kAllToken, rat::kGridHeadRow};
   sp.ntensors = 2;
   sp.B = B; sp.T = T; sp.H = H; sp.Dh = Dh;
   sp.tpad = T;

@@ -112,14 +112,12 @@ struct ScanTensor {
   float* h_last;       // [B][H][Dh] or null
   int all_mode;        // AllMode of out_all
   int grid_mode;       // GridMode of out_grid
-  void* ring;          // window ring [B][H][W][Dh] (input dtype) or null
 };
 
 // Positions.  Row t of the inputs is absolute position p0 + t: grid entries
 // are the states at absolute positions j with (j + 1) % D == 0 (entry
-// (j + 1) / D - 1), all-state outputs put row t at row (or column)
-// all_row0 + t of a buffer with arows rows, and states at absolute
-// positions >= ring_from also go to ring slot j % W.
+// (j + 1) / D - 1), and all-state outputs put row t at row (or column)
+// all_row0 + t of a buffer with arows rows.
 struct ScanPlan {
   ScanTensor ten[2];
   int ntensors;
@@ -128,8 +126,6 @@ struct ScanPlan {
   int64_t p0;          // absolute position of row 0
   int64_t all_row0;    // all-state row of input row 0 (multiple of 64 for kAllHeadCol)
   int64_t arows;       // rows of a kAllToken buffer (>= all_row0 + T)
-  int W;               // ring length (ring outputs only)
-  int64_t ring_from;   // first absolute position written to the ring
   int reset_every;     // > 0: chunk-local recurrence, restarted from zero at multiples of it
   int bf16;            // 1: x and outputs are bf16; 0: fp32
   HeadTable heads;
@@ -167,13 +163,16 @@ hipError_t launch_prefill_attention(const AttnPlan& p, hipStream_t s);
 // ring slot (base + r) % W where base + r >= ring_lo, zeros elsewhere.  K in
 // kAllToken with arows rows; V in kAllHeadCol (bf16) or kAllToken (fp32).
 struct RingPrefixPlan {
-  const void* ring_k; const void* ring_v;   // [B][H][W][Dh]
+  void* ring_k; void* ring_v;               // [B][H][W][Dh]
   void* all_k; void* all_v;
   int B, H, Dh, W;
   int64_t base, n_pre, ring_lo, arows, tpad;
   int bf16;
 };
 hipError_t launch_ring_prefix(const RingPrefixPlan& p, hipStream_t s);
+// The reverse: ring slots of positions [ring_from, base + arows) from the
+// all-state buffers (rows ring_from - base ..).
+hipError_t launch_states_to_ring(const RingPrefixPlan& p, int64_t ring_from, hipStream_t s);
 
 // Grid rows [0, rows[h]) of every (b, h) from the row-major cache layout
 // (heads.goff / heads.gcap) into the column layout (vgoff / vgcap, zero past

@@ -89,6 +89,12 @@ template <> struct XVec<float, 1> {
   __device__ static void hide(raw& r) { opaque(r); }
 };
 
+// a + b for non-negative b, saturating at INT_MAX (row indices past the
+// sequence only need to stay out of reach)
+__device__ __forceinline__ int sat_add(int a, int b) {
+  return a > 0x7fffffff - b ? 0x7fffffff : a + b;
+}
+
 // Stores into the transposed (column) layouts: four consecutive keys of one
 // row, or one key.
 __device__ __forceinline__ void store4(bf16_t* p, const float* v) {
@@ -107,8 +113,6 @@ struct ScanArgs {
   int64_t p0;         // absolute position of input row 0
   int64_t all_row0;   // all-state row of input row 0
   int64_t arows;      // rows of kAllToken outputs
-  int W;              // ring length
-  int64_t ring_from;  // first absolute position stored in the ring
   int reset_every;    // > 0: the state restarts from zero at positions j with j % reset_every == 0
   int n_slabs;        // ntensors * B * slabs_per_bt
   int slabs_per_bt;   // C / (64 * NC)
@@ -141,7 +145,7 @@ __global__ void scan_prologue(uint32_t* hdr) {
 
 // Aggregate (prod g, state from a zero carry) of chunk j for one channel,
 // computed straight from the inputs: the look-back's fallback.
-template <typename XT>
+template <typename XT, bool RESET>
 __device__ void chunk_aggregate(const XT* x, const float* z, int64_t C, int T, int j, int64_t p0, int reset,
                                 float& A, float& Bv) {
   A = 1.f;
@@ -150,7 +154,7 @@ __device__ void chunk_aggregate(const XT* x, const float* z, int64_t C, int T, i
   for (int t = j * kChunkT; t < t_end; ++t) {
     float g, c;
     gate_pair(z[(int64_t)t * C], g, c);
-    if (reset > 0 && (p0 + t) % reset == 0) g = 0.f;   // restart: the carried state is dropped
+    if (RESET && (p0 + t) % reset == 0) g = 0.f;   // restart: the carried state is dropped
     const float xv = sizeof(XT) == 2 ? bf16_to_f32(reinterpret_cast<const bf16_t*>(x)[(int64_t)t * C])
                                      : reinterpret_cast<const float*>(x)[(int64_t)t * C];
     Bv = g * Bv + c * xv;
@@ -158,7 +162,7 @@ __device__ void chunk_aggregate(const XT* x, const float* z, int64_t C, int T, i
   }
 }
 
-template <typename XT, int NC>
+template <typename XT, int NC, bool RESET>
 __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
   using V = XVec<XT, NC>;
   using Z = XVec<float, NC>;
@@ -213,10 +217,11 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
   }
 
   // first restart position >= p0 + t0 (chunk-local recurrence), or none
-  int64_t first_reset = INT64_MAX;
+  // (kept relative to input row 0, as a 32-bit row index; INT_MAX: none)
+  int first_reset = 0x7fffffff;
   if (a.reset_every > 0) {
     const int64_t ja = a.p0 + t0;
-    first_reset = (ja + a.reset_every - 1) / a.reset_every * a.reset_every;
+    first_reset = int(min<int64_t>((ja + a.reset_every - 1) / a.reset_every * a.reset_every - a.p0, 0x7fffffff));
   }
 
   // ---- pass 1: aggregate of the wave's steps (identity past the end)
@@ -224,12 +229,12 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
     float hl[NC], pp[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) { hl[c] = 0.f; pp[c] = 1.f; }
-    int64_t next_reset = first_reset;
+    int next_reset = first_reset;
 #pragma unroll
     for (int s = 0; s < kLW; ++s) {
       const bool live = (t0 + s) < T;
-      const bool rs = a.p0 + t0 + s == next_reset;
-      if (rs) next_reset += a.reset_every;
+      const bool rs = RESET && t0 + s == next_reset;
+      if (rs) next_reset = sat_add(next_reset, a.reset_every);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         float g, cc;
@@ -307,7 +312,7 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
           // predecessor j shows no progress: fold its chunk in directly
           const int chg = cs * SC + cl;
           float Aj, Bj;
-          chunk_aggregate<XT>(static_cast<const XT*>(tn.x) + (int64_t)b * T * C + chg,
+          chunk_aggregate<XT, RESET>(static_cast<const XT*>(tn.x) + (int64_t)b * T * C + chg,
                               tn.z + (int64_t)b * T * C + chg, C, T, j, a.p0, a.reset_every, Aj, Bj);
           accB = accA * Bj + accB;
           accA *= Aj;
@@ -344,8 +349,12 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
   const int D = tn.grid_mode == kGridToken ? a.heads.dil[0] : a.heads.dil[h];
   // first grid position >= p0 + t0 (absolute): smallest j with (j + 1) % D == 0
   const int64_t ja0 = a.p0 + t0;
-  int64_t next_grid = (ja0 / D) * D + (D - 1);
-  if (next_grid < ja0) next_grid += D;
+  int64_t next_grid_abs = (ja0 / D) * D + (D - 1);
+  if (next_grid_abs < ja0) next_grid_abs += D;
+  // row index (relative to input row 0) of the next grid state and its entry
+  int next_grid = int(min<int64_t>(next_grid_abs - a.p0, 0x7fffffff));
+  int64_t grid_i = (next_grid_abs + 1) / D - 1;
+
   XT* out_all = static_cast<XT*>(tn.out_all);
   XT* out_grid = static_cast<XT*>(tn.out_grid);
   const int64_t G_tok = T / D;
@@ -357,13 +366,13 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
   const int64_t col_grid_row = col_grid ? grid_row_offset(a.heads, a.B, b, h, 0, a.Dh) +
                                               (int64_t)d * a.heads.gcap[h] : 0;
   float run[NC][4];
-  int64_t next_reset = first_reset;
+  int next_reset = first_reset;
 
 #pragma unroll
   for (int s = 0; s < kLW; ++s) {
     const int t = t0 + s;
-    const bool rs = a.p0 + t == next_reset;
-    if (rs) next_reset += a.reset_every;
+    const bool rs = RESET && t == next_reset;
+    if (rs) next_reset = sat_add(next_reset, a.reset_every);
     if (t < T) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
@@ -373,8 +382,8 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
         hv[c] = g * hv[c] + cc * V::get(xr[s], c);
       }
       if (tok_all) V::store(out_all + ((int64_t)b * a.arows + a.all_row0 + t) * C + cs * SC + lo, hv);
-      if (out_grid && a.p0 + t == next_grid) {
-        const int64_t i = (a.p0 + t + 1) / D - 1;
+      if (out_grid && t == next_grid) {
+        const int64_t i = grid_i++;
         if (tn.grid_mode == kGridToken) {
           V::store(out_grid + (((int64_t)b * G_tok + i) * a.H + h) * a.Dh + d, hv);
         } else if (tn.grid_mode == kGridHeadRow) {
@@ -384,15 +393,11 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
           for (int c = 0; c < NC; ++c)
             store1(out_grid + col_grid_row + (int64_t)c * a.heads.gcap[h] + col_key_pos(i, d + c), hv[c]);
         }
-        next_grid += D;
+        next_grid = sat_add(next_grid, D);
       }
       if (tn.h_last && t == T - 1) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) tn.h_last[((int64_t)b * a.H + h) * a.Dh + d + c] = hv[c];
-      }
-      if (tn.ring && a.p0 + t >= a.ring_from) {
-        const int64_t slot = (a.p0 + t) % a.W;
-        V::store(static_cast<XT*>(tn.ring) + (((int64_t)b * a.H + h) * a.W + slot) * a.Dh + d, hv);
       }
     }
     if (col_all) {
@@ -455,7 +460,12 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
 template <typename XT, int NC>
 hipError_t launch_typed(const ScanArgs& a, int n_chunks, hipStream_t s) {
   const int blocks = n_chunks * a.n_slabs;
-  hipLaunchKernelGGL((scan_kernel<XT, NC>), dim3(blocks), dim3(kNW * 64), 0, s, a);
+  // the chunk-local restart is a separate instantiation: the plain scan
+  // carries no per-step check for it
+  if (a.reset_every > 0)
+    hipLaunchKernelGGL((scan_kernel<XT, NC, true>), dim3(blocks), dim3(kNW * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((scan_kernel<XT, NC, false>), dim3(blocks), dim3(kNW * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -486,8 +496,6 @@ hipError_t launch_scan(const ScanPlan& p, hipStream_t s) {
   a.p0 = p.p0;
   a.all_row0 = p.all_row0;
   a.arows = p.arows > 0 ? p.arows : p.T;
-  a.W = p.W;
-  a.ring_from = p.ring_from;
   a.reset_every = p.reset_every;
   a.heads = p.heads;
   a.fallback_spins = p.fallback_spins >= 0 ? uint32_t(p.fallback_spins) : kFallbackSpins;
