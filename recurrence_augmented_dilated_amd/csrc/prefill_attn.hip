@@ -24,9 +24,12 @@
 // products.  Tiles stream through a four-stage LDS ring filled by direct
 // global->LDS loads: K rows with XOR-swizzled 16-byte chunks, V from the
 // scan's transposed layout, where one lane's eight keys of a 16-key step are
-// a single 16-byte chunk.  Softmax runs in base 2 with the scale folded into
-// one FMA and tree reductions.  Block order is heaviest q-tile first and
-// keeps each (b, h) pair on one XCD.
+// a single 16-byte chunk; load addresses are a wave-uniform base plus a
+// 32-bit lane offset.  Softmax runs in base 2 with the scale folded into one
+// FMA, a v_maximum3 max tree, a lazily raised running max (the O rescale is
+// rare) and row sums taken by v_dot2 over the same bf16 weights that enter
+// P V.  Block order is heaviest q-tile first and keeps each (b, h) pair on
+// one XCD.
 //
 // fp32 kernel.  A plain exact-fp32 path (one or two lanes per query, keys
 // staged in LDS) for fp32 inputs.
@@ -101,42 +104,43 @@ __device__ __forceinline__ void half_pair(float v, float& lo, float& hi) {
   hi = __uint_as_float(r[1]);
 }
 
-// Max and sum of a lane's 32 scores as balanced trees (short dependency
-// chains; the order of the fp32 sum differs from a left-to-right loop only
-// by rounding).
+// Max of a lane's 32 scores as a v_maximum3 tree (IEEE maximum: no
+// canonicalising copies of the inputs, short dependency chains).
 __device__ __forceinline__ float tree_max32(const floatx16_t* s) {
-  float m[16];
+  auto mx = [](float x, float y) { return __builtin_elementwise_maximum(x, y); };
+  float t[11];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) m[r] = fmaxf(s[0][r], s[1][r]);
-#pragma unroll
-  for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-    for (int r = 0; r < w; ++r) m[r] = fmaxf(m[r], m[r + w]);
-  return m[0];
+  for (int i = 0; i < 10; ++i) {
+    const int e0 = 3 * i, e1 = 3 * i + 1, e2 = 3 * i + 2;
+    t[i] = mx(mx(s[e0 >> 4][e0 & 15], s[e1 >> 4][e1 & 15]), s[e2 >> 4][e2 & 15]);
+  }
+  t[10] = mx(s[1][14], s[1][15]);
+  const float u0 = mx(mx(t[0], t[1]), t[2]);
+  const float u1 = mx(mx(t[3], t[4]), t[5]);
+  const float u2 = mx(mx(t[6], t[7]), t[8]);
+  const float u3 = mx(t[9], t[10]);
+  return mx(mx(u0, u1), mx(u2, u3));
 }
-__device__ __forceinline__ float tree_sum32(const floatx16_t* s) {
-  float m[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) m[r] = s[0][r] + s[1][r];
-#pragma unroll
-  for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-    for (int r = 0; r < w; ++r) m[r] += m[r + w];
-  return m[0];
-}
+
+// Lazy running max (base-2 units): a row's max moves only when a tile holds a
+// score above it by more than kLazy, so every exp2 argument stays <= kLazy
+// and the O rescale is rare.  The final division by the sum taken against the
+// same max makes the result independent of this choice up to rounding.
+constexpr float kLazy = 8.f;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void gbl_void_t;
 
-// 16 bytes per lane straight from global memory into LDS: lane l of the wave
-// writes dst + 16 * l (dst must be wave-uniform).  Written as asm so that the
-// compiler does not treat every later LDS read as dependent on it (it cannot
-// prove the ring stages disjoint and would wait for all loads in flight);
-// the instruction has no destination register, and the kernel waits on
-// vmcnt itself before a stage is read.
-__device__ __forceinline__ void load_lds16(const void* src, void* dst) {
+// 16 bytes per lane straight from global memory at base + voff (a
+// wave-uniform base in an SGPR pair plus a 32-bit per-lane byte offset) into
+// LDS: lane l of the wave writes dst + 16 * l (dst must be wave-uniform).
+// Written as asm so that the compiler does not treat every later LDS read as
+// dependent on it (it cannot prove the ring stages disjoint and would wait
+// for all loads in flight); the instruction has no destination register, and
+// the kernel waits on vmcnt itself before a stage is read.
+__device__ __forceinline__ void load_lds16(const void* base, uint32_t voff, void* dst) {
   const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)dst));
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory");
 }
 
 // Wait until at most n of this wave's vector-memory operations are pending.
@@ -226,33 +230,43 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
   const bf16_t* avt = W > 0 ? static_cast<const bf16_t*>(a.all_v) + ((int64_t)b * H + h) * DH * a.tpad : nullptr;
 
   // issue the direct loads of tile `it` into (dK, dV)
-  auto issue = [&](int it, char* dK, char* dV) __attribute__((always_inline)) {
-    const bf16_t* kb;
-    const bf16_t* vb;
-    int64_t kstride, vstride;
-    int row0, nvalid;
-    if (it < ntile_g) {
-      row0 = it * kBN;
-      kb = gk; kstride = DH; nvalid = ng_hi - row0;
-      vb = gvt; vstride = cap;
-    } else {
-      row0 = j_lo + (it - ntile_g) * kBN - a.base;   // buffer row of the tile
-      kb = ak; kstride = rowC; nvalid = P0 + t_last + 1 - (row0 + a.base);
-      vb = avt; vstride = a.tpad;
-    }
+  // per-lane parts of the direct-load addresses (bytes): K row within the
+  // tile and its chunk; V^T row (grid and window layouts) and chunk
+  int k_row[KL];
+  uint32_t k_chunk[KL], v_off_g[VL], v_off_w[VL];
 #pragma unroll
-    for (int u = 0; u < KL; ++u) {
-      const int j = wave * KL + u;                 // 1 KB slice of the tile
-      const int r = j * (64 / LPR) + lane / LPR;   // key row
-      const int p = lane % LPR;                    // physical 16-byte chunk
-      const int c = p ^ (r & (LPR - 1) & 15);      // logical chunk stored there
-      load_lds16(kb + (int64_t)(row0 + min(r, nvalid - 1)) * kstride + 8 * c, dK + j * 1024);
-    }
+  for (int u = 0; u < KL; ++u) {
+    const int j = wave * KL + u;                 // 1 KB slice of the tile
+    const int r = j * (64 / LPR) + lane / LPR;   // key row
+    const int p = lane % LPR;                    // physical 16-byte chunk
+    k_row[u] = r;
+    k_chunk[u] = 16u * uint32_t(p ^ (r & (LPR - 1) & 15));   // logical chunk stored there
+  }
+#pragma unroll
+  for (int u = 0; u < VL; ++u) {
+    const int j = wave * VL + u;
+    const uint32_t d = uint32_t(j * 8 + lane / 8);             // head-dim row of V^T
+    v_off_g[u] = d * uint32_t(cap) * 2u + 16u * uint32_t(lane % 8);
+    v_off_w[u] = W > 0 ? d * uint32_t(a.tpad) * 2u + 16u * uint32_t(lane % 8) : 0u;
+  }
+  const uint32_t krow_g = DH * 2, krow_w = uint32_t(rowC) * 2u;   // K row strides (bytes)
+
+  // issue the direct loads of tile `it` into (dK, dV); the tile's first row
+  // goes into the wave-uniform base, rows past the last valid one re-read it
+  auto issue = [&](int it, char* dK, char* dV) __attribute__((always_inline)) {
+    const bool isg = it < ntile_g;
+    const int row0 = isg ? it * kBN : j_lo + (it - ntile_g) * kBN - a.base;   // buffer row of the tile
+    const int nvalid = isg ? ng_hi - row0 : P0 + t_last + 1 - (row0 + a.base);
+    const uint32_t krow = isg ? krow_g : krow_w;
+    const char* kb = reinterpret_cast<const char*>(isg ? gk : ak) + (int64_t)row0 * krow;
+    const char* vb = reinterpret_cast<const char*>(isg ? gvt : avt) + (int64_t)row0 * 2;
+#pragma unroll
+    for (int u = 0; u < KL; ++u)
+      load_lds16(kb, uint32_t(min(k_row[u], nvalid - 1)) * krow + k_chunk[u], dK + (wave * KL + u) * 1024);
 #pragma unroll
     for (int u = 0; u < VL; ++u) {
-      const int j = wave * VL + u;
-      const int d = j * 8 + lane / 8;              // head-dim row of V^T
-      load_lds16(vb + (int64_t)d * vstride + row0 + 8 * (lane % 8), dV + j * 1024);
+      const uint32_t og = v_off_g[u], ow = v_off_w[u];
+      load_lds16(vb, isg ? og : ow, dV + (wave * VL + u) * 1024);
     }
   };
 
@@ -303,63 +317,67 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
     if (!needed) return;
     // ---- mask: key index kbase + c(kb, r) + 4g, branch-free selects
     if (masked) {
-      if (is_grid) {
-        // valid while the grid index is below this query's count
-        const int thr = ng_me - kbase - 4 * g;
+      // key kbase + 4g + c is valid iff lo <= c <= hi: grid keys below this
+      // query's count, window keys in [max(0, t-W+1), t]; one unsigned
+      // range compare per score
+      const int key0 = kbase + 4 * g;
+      const int lo = is_grid ? -64 : win_lo_me - key0;
+      const int hi = is_grid ? ng_me - 1 - key0 : tqa - key0;
+      const bool none = hi < lo;
+      const int lo2 = none ? 1 << 20 : lo;
+      const uint32_t span = none ? 0u : uint32_t(hi - lo);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
-            s[kb][r] = c < thr ? s[kb][r] : -INFINITY;
-          }
-      } else {
-        // valid inside [max(0, t-W+1), t]: one unsigned range compare
-        const int lo = win_lo_me - kbase - 4 * g;
-        const uint32_t span = uint32_t(tqa - win_lo_me);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
-            s[kb][r] = uint32_t(c - lo) <= span ? s[kb][r] : -INFINITY;
-          }
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
+          s[kb][r] = uint32_t(c - lo2) <= span ? s[kb][r] : -INFINITY;
+        }
     }
 
     // ---- online softmax (base 2; running max shared by the two lane halves)
-    float mx, mx_lo, mx_hi;
+    float mx_lo, mx_hi;
     half_pair(tree_max32(s), mx_lo, mx_hi);
-    mx = fmaxf(mx_lo, mx_hi);
-    const float m_new = fmaxf(m_run, mx * a.sl2);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    // rescale only when some row of the wave raised its running max
-    if (__ballot(m_new != m_run) != 0) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    const float mt = __builtin_elementwise_maximum(mx_lo, mx_hi) * a.sl2;
+    const bool up = mt > m_run + kLazy;
+    if (__ballot(up) != 0) {
+      const float m_new = up ? mt : m_run;
+      const float alpha = up ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < DB; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+      m_run = m_new;
     }
-    m_run = m_new;
+    const float nm = m_run == -INFINITY ? 0.f : -m_run;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], a.sl2, -m_use));
-    l_run += tree_sum32(s);
+      for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], a.sl2, nm));
 
-    // ---- O^T += V^T P^T over four 16-key steps
+    // ---- bf16 P^T fragments; row sums over the same rounded weights
+    uint4 pws[4];
+    float lp0 = 0.f, lp1 = 0.f;
+    const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int kb = st >> 1;
       const int r0 = 8 * (st & 1);
-      uint4 pw;
-      pw.x = pack_bf16x2(s[kb][r0 + 0], s[kb][r0 + 1]);
-      pw.y = pack_bf16x2(s[kb][r0 + 2], s[kb][r0 + 3]);
-      pw.z = pack_bf16x2(s[kb][r0 + 4], s[kb][r0 + 5]);
-      pw.w = pack_bf16x2(s[kb][r0 + 6], s[kb][r0 + 7]);
-      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
+      pws[st].x = pack_bf16x2(s[kb][r0 + 0], s[kb][r0 + 1]);
+      pws[st].y = pack_bf16x2(s[kb][r0 + 2], s[kb][r0 + 3]);
+      pws[st].z = pack_bf16x2(s[kb][r0 + 4], s[kb][r0 + 5]);
+      pws[st].w = pack_bf16x2(s[kb][r0 + 6], s[kb][r0 + 7]);
+      lp0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pws[st].x), ones, lp0, false);
+      lp1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pws[st].y), ones, lp1, false);
+      lp0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pws[st].z), ones, lp0, false);
+      lp1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pws[st].w), ones, lp1, false);
+    }
+    l_run += lp0 + lp1;
+    // ---- O^T += V^T P^T over four 16-key steps
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pws[st]);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int d = 32 * db + n;
