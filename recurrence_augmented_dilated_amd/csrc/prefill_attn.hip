@@ -296,16 +296,27 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
   // S^T = K Q^T of one tile into sc (two 32-key blocks)
   auto scores = [&](const char* cK, floatx16_t* sc) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int m = 32 * kb + n;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
+    // the two 32-key chains interleaved; each K read leads its MFMA by
+    // several others
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int m = 32 * kb + n;
         const int c = (2 * ks + g) ^ (m & (LPR - 1) & 15);
         const uint4 w = *reinterpret_cast<const uint4*>(cK + m * KROW + 16 * c);
         sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), qf[ks], sc[kb], 0, 0, 0);
       }
+    constexpr int NM = 2 * KS, LEAD = 6;
+#pragma unroll
+    for (int i = 0; i < LEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + LEAD < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
 
@@ -333,6 +344,15 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
           const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
           s[kb][r] = uint32_t(c - lo2) <= span ? s[kb][r] : -INFINITY;
         }
+    }
+
+    // V^T fragments of the first two 16-key steps, read before the softmax
+    // so that their latency hides under it
+    uint4 vpre[2 * DB];
+#pragma unroll
+    for (int j = 0; j < 2 * DB; ++j) {
+      const int st = j / DB, d = 32 * (j % DB) + n;
+      vpre[j] = *reinterpret_cast<const uint4*>(cV + d * (kBN * 2) + 16 * ((2 * st + g) ^ col_swz(d)));
     }
 
     // ---- online softmax (base 2; running max shared by the two lane halves)
@@ -382,7 +402,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
       for (int db = 0; db < DB; ++db) {
         const int d = 32 * db + n;
         // keys 16st + 4g + {0..3} and 16st + 8 + 4g + {0..3}: one 16-byte chunk
-        const uint4 vw = *reinterpret_cast<const uint4*>(cV + d * (kBN * 2) + 16 * ((2 * st + g) ^ col_swz(d)));
+        const uint4 vw = st < 2 ? vpre[st * DB + db]
+                                : *reinterpret_cast<const uint4*>(cV + d * (kBN * 2) + 16 * ((2 * st + g) ^ col_swz(d)));
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vw), pf, o[db], 0, 0, 0);
       }
     }

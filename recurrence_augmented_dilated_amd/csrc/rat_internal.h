@@ -44,6 +44,15 @@ __device__ __forceinline__ void gate_pair(float z, float& g, float& c) {
   g = pos ? big : small;
   c = pos ? small : big;
 }
+// sigmoid(-z) = 1 - g by itself, the input weight of the recurrence.  The
+// prefill scan keeps only this value per element and takes the decay as one
+// minus it: one rounding, an absolute error near 1e-7 that is relatively
+// large only where the decay itself is negligible.
+__device__ __forceinline__ float gate_comp(float z) {
+  const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * fabsf(z));
+  const float big = __builtin_amdgcn_rcpf(1.0f + e);
+  return z >= 0.0f ? e * big : big;
+}
 
 // ---------------------------------------------------------------------------
 // Per-head tables, passed by value as kernel arguments.

@@ -10,12 +10,12 @@
 // owns NC adjacent channels and walks time sequentially; a wave covers 64*NC
 // channels and kLW time steps; a block of kNW waves covers kNW*kLW steps (a
 // "chunk") of one channel slab.  Every input element is read from HBM once
-// and kept in registers as loaded (bf16/fp32 x, fp32 z): a first pass folds
-// the wave's steps into an aggregate (A = prod g, B = state reached from a
-// zero carry), and once the chunk's carry-in is known a second pass re-runs
-// the recurrence from it over the same registers and stores the states.
-// Recomputing the gates costs VALU work but halves the registers a step
-// needs, which keeps enough waves resident to hide the look-back latency.
+// and kept in registers as loaded (bf16/fp32 x, fp32 z): a first pass turns
+// every z into 1 - g in place and folds the wave's steps into an aggregate
+// (A = prod g, B = state reached from a zero carry), and once the chunk's
+// carry-in is known a second pass re-runs the recurrence from it over the
+// same registers (g = 1 - (1 - g): one subtraction per element, no second
+// sigmoid) and stores the states.
 //
 // Carry propagation across chunks is a decoupled look-back.  Block b of the
 // grid handles chunk b / n_slabs of slab b % n_slabs, publishes its chunk
@@ -79,6 +79,7 @@ template <> struct XVec<float, 2> {
   }
   __device__ static raw zero() { return make_float2(0.f, 0.f); }
   __device__ static void hide(raw& r) { opaque(r.x); opaque(r.y); }
+  __device__ static void set(raw& r, int c, float v) { (c ? r.y : r.x) = v; }
 };
 template <> struct XVec<float, 1> {
   using raw = float;
@@ -87,6 +88,7 @@ template <> struct XVec<float, 1> {
   __device__ static void store(float* p, const float* v) { *p = v[0]; }
   __device__ static raw zero() { return 0.f; }
   __device__ static void hide(raw& r) { opaque(r); }
+  __device__ static void set(raw& r, int, float v) { r = v; }
 };
 
 // a + b for non-negative b, saturating at INT_MAX (row indices past the
@@ -152,8 +154,8 @@ __device__ void chunk_aggregate(const XT* x, const float* z, int64_t C, int T, i
   Bv = 0.f;
   const int t_end = min(T, (j + 1) * kChunkT);
   for (int t = j * kChunkT; t < t_end; ++t) {
-    float g, c;
-    gate_pair(z[(int64_t)t * C], g, c);
+    const float c = gate_comp(z[(int64_t)t * C]);
+    float g = 1.f - c;
     if (RESET && (p0 + t) % reset == 0) g = 0.f;   // restart: the carried state is dropped
     const float xv = sizeof(XT) == 2 ? bf16_to_f32(reinterpret_cast<const bf16_t*>(x)[(int64_t)t * C])
                                      : reinterpret_cast<const float*>(x)[(int64_t)t * C];
@@ -237,8 +239,9 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
       if (rs) next_reset = sat_add(next_reset, a.reset_every);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        float g, cc;
-        gate_pair(Z::get(zr[s], c), g, cc);
+        float cc = gate_comp(Z::get(zr[s], c));
+        Z::set(zr[s], c, cc);   // pass 2 reads 1 - g from here
+        float g = 1.f - cc;
         if (rs) g = 0.f;
         if (!live) { g = 1.f; cc = 0.f; }
         hl[c] = g * hl[c] + cc * V::get(xr[s], c);
@@ -339,7 +342,9 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
   }
   __syncthreads();
 
-  // ---- pass 2: the recurrence from the carry-in; stores
+  // ---- pass 2: the recurrence from the carry-in (1 - g kept from pass 1);
+  // stores.  The registers are hidden from the optimiser so that it does not
+  // keep pass 1's gates alive across the look-back instead.
 #pragma unroll
   for (int s = 0; s < kLW; ++s) { V::hide(xr[s]); Z::hide(zr[s]); }
   float hv[NC];
@@ -376,8 +381,8 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
     if (t < T) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        float g, cc;
-        gate_pair(Z::get(zr[s], c), g, cc);
+        const float cc = Z::get(zr[s], c);
+        float g = 1.f - cc;
         if (rs) g = 0.f;   // chunk start: the state restarts from zero
         hv[c] = g * hv[c] + cc * V::get(xr[s], c);
       }
