@@ -412,9 +412,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
   constexpr int LPW = KL + VL;   // direct loads per wave per tile
   constexpr int kAhead = 3;      // tiles in flight ahead of the one consumed
   floatx16_t sc[2];
-  auto step = [&](int it) __attribute__((always_inline)) {
-    const bool pre = it + kAhead < ntiles;
-    if (pre) issue(it + kAhead, sK[(it + kAhead) & 3], sV[(it + kAhead) & 3]);
+  auto tile = [&](int it) __attribute__((always_inline)) {
     bool is_grid, needed, masked;
     int kbase;
     tile_info(it, is_grid, needed, masked, kbase);
@@ -422,24 +420,50 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
       scores(sK[it & 3], sc);
       finish(it, sV[it & 3], sc);
     }
-    // tile it+1 must have landed; later tiles may still fly
-    const int later = min(ntiles - 1, it + kAhead) - (it + 1);
-    if (later >= 2) wait_vmcnt<2 * LPW>();
-    else if (later == 1) wait_vmcnt<LPW>();
-    else wait_vmcnt<0>();
-    ring_barrier();
   };
 
   wait_vmcnt<0>();   // Q fragments are in registers before the ring starts
-  for (int p = 0; p < kAhead && p < ntiles; ++p) issue(p, sK[p], sV[p]);
-  if (ntiles > 0) {
-    const int later = min(ntiles, kAhead) - 1;   // tiles issued after tile 0
-    if (later >= 2) wait_vmcnt<2 * LPW>();
-    else if (later == 1) wait_vmcnt<LPW>();
-    else wait_vmcnt<0>();
-    ring_barrier();
+  if (W > 0) {
+    // With a window band every wave skips some of the block's window tiles,
+    // so tiles go in pairs between barriers: while pair p is consumed, pair
+    // p+1 lands in the other half of the ring (the slots of pair p-1, free
+    // since the last barrier), and a wave that skips one tile of a pair goes
+    // straight on to the other.
+    for (int p = 0; p < 2 && p < ntiles; ++p) issue(p, sK[p], sV[p]);
+    if (ntiles > 0) {
+      wait_vmcnt<0>();
+      ring_barrier();
+    }
+    for (int t0 = 0; t0 < ntiles; t0 += 2) {
+#pragma unroll
+      for (int q = 2; q < 4; ++q)
+        if (t0 + q < ntiles) issue(t0 + q, sK[(t0 + q) & 3], sV[(t0 + q) & 3]);
+      tile(t0);
+      if (t0 + 1 < ntiles) tile(t0 + 1);
+      wait_vmcnt<0>();
+      ring_barrier();
+    }
+  } else {
+    // one tile per barrier, three in flight
+    for (int p = 0; p < kAhead && p < ntiles; ++p) issue(p, sK[p], sV[p]);
+    if (ntiles > 0) {
+      const int later = min(ntiles, kAhead) - 1;   // tiles issued after tile 0
+      if (later >= 2) wait_vmcnt<2 * LPW>();
+      else if (later == 1) wait_vmcnt<LPW>();
+      else wait_vmcnt<0>();
+      ring_barrier();
+    }
+    for (int it = 0; it < ntiles; ++it) {
+      if (it + kAhead < ntiles) issue(it + kAhead, sK[(it + kAhead) & 3], sV[(it + kAhead) & 3]);
+      tile(it);
+      // tile it+1 must have landed; later tiles may still fly
+      const int later = min(ntiles - 1, it + kAhead) - (it + 1);
+      if (later >= 2) wait_vmcnt<2 * LPW>();
+      else if (later == 1) wait_vmcnt<LPW>();
+      else wait_vmcnt<0>();
+      ring_barrier();
+    }
   }
-  for (int it = 0; it < ntiles; ++it) step(it);
 
   // ---- normalise and store (empty key set -> zeros)
   float l_lo, l_hi;
