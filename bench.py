@@ -324,16 +324,17 @@ def bench_topk_decode(c, steps, warmup, torch, R):
 
 
 def topk_prefill_flops(c):
-    """fp32 VALU flops of top-k block prefill attention: scoring every
-    candidate block and the softmax attention over the kept positions."""
+    """Flops of top-k block prefill: (scoring every candidate block, the
+    softmax attention over the kept positions, 4 Dh per kept pair)."""
     B, H, Dh, T, blk, k = c["B"], c["H"], c["Dh"], c["T"], c["block"], c["topk"]
-    total = 0
+    score = attn = 0
     for t in range(T):
         local = t // blk
         ncand = max(0, local - 1)
         kept = min(k, ncand) * blk + (blk if local > 0 else 0) + (t - local * blk + 1)
-        total += (2 * Dh if c["score"] == 1 else 3 * Dh) * ncand + 4 * Dh * kept
-    return B * H * total
+        score += (2 * Dh if c["score"] == 1 else 3 * Dh) * ncand
+        attn += 4 * Dh * kept
+    return B * H * score, B * H * attn
 
 
 def bench_topk_prefill(c, steps, warmup, torch, R, inputs):
@@ -422,15 +423,16 @@ def aux_result(cfg_id, c, a, torch, R, inputs):
                    ws_error=err)
     elif kind == "topk_prefill":
         ms = bench_topk_prefill(c, a.steps, a.warmup, torch, R, inputs)
-        fl = topk_prefill_flops(c)
+        _, fl = topk_prefill_flops(c)
         res.update(metric="top-k block attention prefill tokens/s", value=c["B"] * c["T"] / (ms * 1e-3),
                    ms_per_step=ms,
                    config={"workload": f"top-k prefill B={c['B']} H={c['H']} Dh={c['Dh']} T={c['T']} "
                                        f"block={c['block']} topk={c['topk']} {'quest' if c['score'] == 0 else 'moba'}",
                            "config_id": cfg_id},
-                   roofline={"kernel": "whole step (recurrence + summaries + select + attend)", "bound": "alu",
-                             "achieved": fl / (ms * 1e-3) / 1e12, "peak": PEAK_F32_VALU / 1e12, "unit": "TFLOP/s",
-                             "frac": fl / (ms * 1e-3) / PEAK_F32_VALU, "traffic": None})
+                   roofline={"kernel": "whole step (recurrence + summaries + select + attend)", "bound": "mfma",
+                             "achieved": fl / (ms * 1e-3) / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                             "frac": fl / (ms * 1e-3) / PEAK_BF16, "traffic": None,
+                             "note": "attention flops of the kept (query, key) pairs over the whole step time"})
     return res
 
 

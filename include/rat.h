@@ -290,7 +290,11 @@ typedef enum { RAT_TOPK_QUEST = 0, RAT_TOPK_MOBA = 1 } rat_topk_score_t;
  * sequences whose positions before p0 are cached: recurrence from state_k/_v,
  * every new state into the caches, summaries of the blocks completed, then
  * top-k block attention for every row.  q, k, v, zk, zv, out as
- * rat_dilated_prefill; chosen [B][T][H][topk] or NULL. */
+ * rat_dilated_prefill; chosen [B][T][H][topk] or NULL.  bf16 calls with
+ * block = 64, topk <= 16 and p0 = 0 select first and then run the MFMA
+ * prefill attention over the cache with the per-query block sets (the
+ * workspace then also holds the transposed values and the chosen lists);
+ * other calls take one workgroup per query. */
 size_t rat_topk_prefill_workspace_size(int32_t B, int32_t T, int32_t H, int32_t Dh);
 rat_status_t rat_topk_prefill(const void* q, const void* k, const void* v, const float* zk,
                               const float* zv, void* out, int32_t* chosen, float* state_k,

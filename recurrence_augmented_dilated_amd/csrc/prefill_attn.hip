@@ -59,6 +59,8 @@ struct AttnArgs {
   HeadTable heads;            // dilation; grid keys at goff / gcap
   int64_t vgoff[kMaxHeads];   // grid values: element offset B * vgoff[h] * Dh
   int32_t vgcap[kMaxHeads];   // grid values: capacity (row length in kGridHeadCol)
+  const int32_t* sel;         // block-selection mode: chosen blocks [B][T][H][sel_k]
+  int sel_k;
 };
 static_assert(sizeof(AttnArgs) <= 4096, "kernel argument size");
 
@@ -161,7 +163,11 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int DH>
+// SEL: block-selection key set (top-k block attention): block 0, the query's
+// own block and its chosen blocks, 64 positions per block = one tile; the
+// per-query lists sit in LDS and every lane walks its query's list as the
+// block index grows.
+template <int DH, bool SEL>
 __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArgs a) {
   constexpr int KS = DH / 16;                 // MFMA k-steps over the head dim
   constexpr int DB = DH / 32;                 // 32-wide d blocks of O^T
@@ -223,9 +229,12 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
   const int ng_w0 = wave_live ? n_grid(tw0, W, D) : 0;
   const int ng_w1 = wave_live ? n_grid(tw1, W, D) : 0;
 
-  const int cap = a.vgcap[h];             // row length of the transposed grid values
+  // row length of the transposed grid values; in block-selection mode the
+  // values are kAllHeadCol rows of tpad columns
+  const int cap = SEL ? int(a.tpad) : a.vgcap[h];
   const bf16_t* gk = static_cast<const bf16_t*>(a.grid_k) + grid_row_offset(a.heads, a.B, b, h, 0, DH);
-  const bf16_t* gvt = static_cast<const bf16_t*>(a.grid_v) + ((int64_t)a.B * a.vgoff[h] + (int64_t)b * cap) * DH;
+  const bf16_t* gvt = static_cast<const bf16_t*>(a.grid_v) +
+                      (SEL ? ((int64_t)b * H + h) * DH * a.tpad : ((int64_t)a.B * a.vgoff[h] + (int64_t)b * cap) * DH);
   const bf16_t* ak = W > 0 ? static_cast<const bf16_t*>(a.all_k) + (int64_t)b * a.arows * rowC + h * DH : nullptr;
   const bf16_t* avt = W > 0 ? static_cast<const bf16_t*>(a.all_v) + ((int64_t)b * H + h) * DH * a.tpad : nullptr;
 
@@ -280,9 +289,30 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
 
   // needed: does any query of this wave see a key of tile it?
   // masked: does some (query, key) pair of the tile fall outside the key set?
+  // block-selection mode: is block it in this lane's query's key set
+  constexpr int kSelStride = kSelMaxK + 1;   // list entries plus a -1 sentinel
+  __shared__ int32_t s_sel[SEL ? kBM * kSelStride : 1];
+  bool lane_sel = true;
+  int sel_ptr = 0, sel_nxt = -1;
+  const int sel_row = (wave * 32 + n) * kSelStride;
+  const int own_blk = tqa / kBN;
+  auto sel_advance = [&](int it) __attribute__((always_inline)) {
+    const bool hit = sel_nxt == it;
+    lane_sel = (it == 0) | (it == own_blk) | hit;
+    sel_ptr += hit ? 1 : 0;
+    sel_nxt = s_sel[sel_row + sel_ptr];
+  };
+
   auto tile_info = [&](int it, bool& is_grid, bool& needed, bool& masked, int& kbase) __attribute__((always_inline)) {
     is_grid = it < ntile_g;
-    if (is_grid) {
+    if (SEL) {
+      // grid tiles only (D = 1, W = 0); skip a tile no query of the wave
+      // keeps, mask it unless every query keeps it
+      kbase = it * kBN;
+      const uint64_t keep = __ballot(lane_sel && q_live && kbase < ng_me);
+      needed = keep != 0;
+      masked = kbase + kBN > ng_w0 || keep != __ballot(q_live);
+    } else if (is_grid) {
       kbase = it * kBN;
       needed = wave_live && kbase < ng_w1;
       masked = kbase + kBN > ng_w0;
@@ -334,7 +364,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
       const int key0 = kbase + 4 * g;
       const int lo = is_grid ? -64 : win_lo_me - key0;
       const int hi = is_grid ? ng_me - 1 - key0 : tqa - key0;
-      const bool none = hi < lo;
+      const bool none = hi < lo || !lane_sel;
       const int lo2 = none ? 1 << 20 : lo;
       const uint32_t span = none ? 0u : uint32_t(hi - lo);
 #pragma unroll
@@ -444,6 +474,15 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
       ring_barrier();
     }
   } else {
+    if constexpr (SEL) {
+      // the block's chosen lists into LDS (made visible by the barrier below)
+      for (int e = tid; e < kBM * kSelStride; e += kWaves * 64) {
+        const int qi = e / kSelStride, j = e - qi * kSelStride;
+        const int tr = t0 + qi;
+        s_sel[e] = (j < a.sel_k && tr < T) ? a.sel[(((int64_t)b * T + tr) * H + h) * a.sel_k + j] : -1;
+      }
+      wait_vmcnt<0>();
+    }
     // one tile per barrier, three in flight
     for (int p = 0; p < kAhead && p < ntiles; ++p) issue(p, sK[p], sV[p]);
     if (ntiles > 0) {
@@ -453,8 +492,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
       else wait_vmcnt<0>();
       ring_barrier();
     }
+    if constexpr (SEL) sel_nxt = s_sel[sel_row];
     for (int it = 0; it < ntiles; ++it) {
       if (it + kAhead < ntiles) issue(it + kAhead, sK[(it + kAhead) & 3], sV[(it + kAhead) & 3]);
+      if constexpr (SEL) sel_advance(it);
       tile(it);
       // tile it+1 must have landed; later tiles may still fly
       const int later = min(ntiles - 1, it + kAhead) - (it + 1);
@@ -613,6 +654,8 @@ hipError_t launch_prefill_attention(const AttnPlan& p, hipStream_t s) {
   a.arows = p.arows > 0 ? p.arows : p.T;
   a.sl2 = p.scale * 1.4426950408889634f;
   a.heads = p.heads;
+  a.sel = p.sel;
+  a.sel_k = p.sel_k;
   for (int h = 0; h < kMaxHeads; ++h) {
     a.vgoff[h] = p.vgoff[h];
     a.vgcap[h] = p.vgcap[h];
@@ -621,10 +664,16 @@ hipError_t launch_prefill_attention(const AttnPlan& p, hipStream_t s) {
   if (p.bf16) {
     a.n_qtiles = (p.T + kBM - 1) / kBM;
     const int blocks = xcd_padded_blocks(BH, a.n_qtiles);
-    if (p.Dh == 128)
-      hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(blocks), dim3(kWaves * 64), 0, s, a);
-    else
-      hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(blocks), dim3(kWaves * 64), 0, s, a);
+    if (p.sel) {
+      if (p.Dh == 128)
+        hipLaunchKernelGGL((attn_bf16_kernel<128, true>), dim3(blocks), dim3(kWaves * 64), 0, s, a);
+      else
+        hipLaunchKernelGGL((attn_bf16_kernel<64, true>), dim3(blocks), dim3(kWaves * 64), 0, s, a);
+    } else if (p.Dh == 128) {
+      hipLaunchKernelGGL((attn_bf16_kernel<128, false>), dim3(blocks), dim3(kWaves * 64), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((attn_bf16_kernel<64, false>), dim3(blocks), dim3(kWaves * 64), 0, s, a);
+    }
   } else {
     a.n_qtiles = (p.T + 63) / 64;
     const int blocks = xcd_padded_blocks(BH, a.n_qtiles);

@@ -631,7 +631,11 @@ extern "C" {
 
 size_t rat_topk_prefill_workspace_size(int32_t B, int32_t T, int32_t H, int32_t Dh) {
   if (check_common(B, T, H, Dh, RAT_BF16) != RAT_OK) return 0;
-  return align_up(rat::scan_workspace_bytes(2, B, T, H, Dh)) + align_up((size_t)2 * B * H * Dh * sizeof(float));
+  // scan workspace, h0 copies, and for the bf16 block-selection path the
+  // values in kAllHeadCol layout plus the chosen lists
+  const int64_t tpad = (T + 63) / 64 * 64;
+  return align_up(rat::scan_workspace_bytes(2, B, T, H, Dh)) + align_up((size_t)2 * B * H * Dh * sizeof(float)) +
+         align_up((size_t)B * H * Dh * tpad * 2) + align_up((size_t)B * T * H * rat::kSelMaxK * sizeof(int32_t));
 }
 
 rat_status_t rat_topk_prefill(const void* q, const void* k, const void* v, const float* zk,
@@ -663,6 +667,15 @@ rat_status_t rat_topk_prefill(const void* q, const void* k, const void* v, const
   float* h0k = reinterpret_cast<float*>(static_cast<char*>(ws) + scan_bytes);
   float* h0v = h0k + (size_t)B * H * Dh;
   const size_t sbytes = (size_t)B * H * Dh * sizeof(float);
+  // Block-selection path: a first pass writes every query's chosen blocks,
+  // then the MFMA prefill attention runs over the dense cache with the key
+  // set block 0 + chosen + own block (64-position blocks = its key tiles).
+  // It needs the values transposed (written by the scan alongside the cache)
+  // and so starts at position 0; other calls take one workgroup per query.
+  const bool fast = bf16 && block == 64 && topk <= rat::kSelMaxK && p0 == 0;
+  const int64_t tpad = (T + 63) / 64 * 64;
+  char* vcol = reinterpret_cast<char*>(h0k) + align_up(2 * sbytes);
+  int32_t* sel = reinterpret_cast<int32_t*>(vcol + align_up((size_t)B * H * Dh * tpad * 2));
   hipError_t e = hipMemcpyAsync(h0k, state_k, sbytes, hipMemcpyDeviceToDevice, stream);
   if (e == hipSuccess) e = hipMemcpyAsync(h0v, state_v, sbytes, hipMemcpyDeviceToDevice, stream);
   if (e != hipSuccess) return fail(RAT_ERR_HIP, "state copy: %s", hipGetErrorString(e));
@@ -671,10 +684,11 @@ rat_status_t rat_topk_prefill(const void* q, const void* k, const void* v, const
   rat::ScanPlan sp;
   std::memset(&sp, 0, sizeof(sp));
   sp.ten[0] = {k, zk, h0k, nullptr, cache_k, state_k, rat::kAllToken, rat::kGridHeadRow};
-  sp.ten[1] = {v, zv, h0v, nullptr, cache_v, state_v, rat::kAllToken, rat::kGridHeadRow};
+  sp.ten[1] = {v, zv, h0v, fast ? vcol : nullptr, cache_v, state_v,
+               fast ? rat::kAllHeadCol : rat::kAllToken, rat::kGridHeadRow};
   sp.ntensors = 2;
   sp.B = B; sp.T = T; sp.H = H; sp.Dh = Dh;
-  sp.tpad = T;
+  sp.tpad = fast ? tpad : T;
   sp.p0 = p0;
   sp.arows = T;
   sp.bf16 = bf16;
@@ -697,7 +711,29 @@ rat_status_t rat_topk_prefill(const void* q, const void* k, const void* v, const
   const int64_t j_hi = (p0 + T) / block;                 // j with (j + 1) * block <= p0 + T
   e = rat::launch_topk_stats(tp, j_lo, j_hi, stream);
   if (e != hipSuccess) return fail(RAT_ERR_HIP, "block summary launch: %s", hipGetErrorString(e));
+  if (!fast) {
+    e = rat::launch_topk_attend(tp, stream);
+    if (e != hipSuccess) return fail(RAT_ERR_HIP, "top-k attention launch: %s", hipGetErrorString(e));
+    return ok();
+  }
+  int32_t* lists = chosen ? chosen : sel;
+  tp.chosen = lists;
+  tp.select_only = 1;
   e = rat::launch_topk_attend(tp, stream);
+  if (e != hipSuccess) return fail(RAT_ERR_HIP, "top-k selection launch: %s", hipGetErrorString(e));
+  rat::AttnPlan ap;
+  std::memset(&ap, 0, sizeof(ap));
+  ap.q = q; ap.out = out;
+  ap.grid_k = cache_k; ap.grid_v = vcol;
+  ap.B = B; ap.T = T; ap.H = H; ap.Dh = Dh; ap.W = 0;
+  ap.tpad = tpad;
+  ap.arows = T;
+  ap.bf16 = 1;
+  ap.scale = tp.scale;
+  dense_cache_table(H, max_pos, ap.heads);
+  ap.sel = lists;
+  ap.sel_k = topk;
+  e = rat::launch_prefill_attention(ap, stream);
   if (e != hipSuccess) return fail(RAT_ERR_HIP, "top-k attention launch: %s", hipGetErrorString(e));
   return ok();
 }

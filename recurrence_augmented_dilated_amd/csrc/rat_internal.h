@@ -164,7 +164,16 @@ struct AttnPlan {
   HeadTable heads;
   int64_t vgoff[kMaxHeads];
   int32_t vgcap[kMaxHeads];
+  // Block-selection mode (top-k prefill, bf16 only): null for the dilated key
+  // set.  Otherwise the key set of a query is block 0, its own 64-position
+  // block (causal) and the blocks listed for it in sel [B][T][H][sel_k]
+  // (ascending, -1 padded); heads use D = 1 and W = 0, grid_k is the dense
+  // key cache and grid_v the values in kAllHeadCol layout with tpad columns.
+  const int32_t* sel;
+  int sel_k;
 };
+// Largest top-k of the block-selection mode (its per-query lists sit in LDS).
+constexpr int kSelMaxK = 16;
 hipError_t launch_prefill_attention(const AttnPlan& p, hipStream_t s);
 
 // Chunked prefill helpers.
@@ -245,6 +254,7 @@ struct TopkPlan {
   int bf16;
   float scale;
   uint32_t* hdr;        // decode: workspace header (error word)
+  int select_only;      // prefill: write chosen, skip the attention
 };
 // Summaries of the blocks j in [j_lo, j_hi) of every (h, b).
 hipError_t launch_topk_stats(const TopkPlan& p, int64_t j_lo, int64_t j_hi, hipStream_t s);

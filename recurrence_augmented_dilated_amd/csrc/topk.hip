@@ -119,6 +119,10 @@ __device__ __forceinline__ bool better(float v, int j, float bv, int bi) {
   return v == v && (v > bv || (v == bv && j < bi));
 }
 
+// Candidate counts up to this are selected by rank in one pass; larger ones
+// by repeated wave-wide argmax.
+constexpr int kRankMax = 1024;
+
 // ---- selection and attention: one workgroup per query
 template <typename ET, int DH>
 __global__ __launch_bounds__(kAW * 64) void topk_attend_kernel(const TopkPlan p) {
@@ -128,6 +132,7 @@ __global__ __launch_bounds__(kAW * 64) void topk_attend_kernel(const TopkPlan p)
   __shared__ float s_q[DH];
   extern __shared__ float s_sc[];     // candidate scores: max_pos / block floats (launch-time size)
   __shared__ int s_list[kTopkMaxK + 2];
+  __shared__ int16_t s_rank[kRankMax];
   __shared__ float s_m[kAW], s_l[kAW];
   __shared__ float s_acc[kAW][DH];
 
@@ -175,6 +180,7 @@ __global__ __launch_bounds__(kAW * 64) void topk_attend_kernel(const TopkPlan p)
 #pragma unroll
     for (int i = 0; i < 8; ++i) qd[i] = s_q[8 * c + i];
     const int slot = wave * KPW + rg;                 // candidate slot of this lane group
+#pragma unroll 4
     for (int j0 = 0; j0 < ncand; j0 += kAW * KPW) {
       const int j = j0 + slot;
       const bool ok = j < ncand;
@@ -205,6 +211,28 @@ __global__ __launch_bounds__(kAW * 64) void topk_attend_kernel(const TopkPlan p)
   const int nsel = ncand < p.topk ? ncand : p.topk;
   if (ncand <= p.topk) {
     for (int j = tid; j < ncand; j += kAW * 64) s_list[1 + j] = j + 1;
+  } else if (ncand <= kRankMax) {
+    // rank of every candidate: the number that beat it (higher score, ties
+    // to the lower index); the kept ones are the ranks below nsel
+    for (int j = tid; j < ncand; j += kAW * 64) {
+      const float v = s_sc[j];
+      int r = 0;
+      for (int i = 0; i < ncand; ++i) {
+        const float u = s_sc[i];
+        r += (u > v || (u == v && i < j)) ? 1 : 0;
+      }
+      s_rank[j] = (int16_t)r;
+    }
+    __syncthreads();
+    // in ascending block order: a kept candidate's slot counts the kept
+    // candidates below it
+    for (int j = tid; j < ncand; j += kAW * 64) {
+      if (s_rank[j] < nsel) {
+        int pos = 0;
+        for (int i = 0; i < j; ++i) pos += s_rank[i] < nsel ? 1 : 0;
+        s_list[1 + pos] = j + 1;
+      }
+    }
   } else if (wave == 0) {
     for (int r = 0; r < nsel; ++r) {
       float bv = -INFINITY;
@@ -237,6 +265,7 @@ __global__ __launch_bounds__(kAW * 64) void topk_attend_kernel(const TopkPlan p)
   }
   __syncthreads();
   if (cp && tid < p.topk) cp[tid] = tid < nsel ? s_list[1 + tid] : -1;
+  if (p.select_only) return;
 
   // ---- key blocks: first, chosen, local (block 0 alone when local == 0)
   const int nlist = local > 0 ? nsel + 2 : 1;

@@ -186,3 +186,90 @@ def test_topk_summarize_matches_block_statistics():
         for i, ref in enumerate((kmin, kmax, kmean)):
             assert np.max(np.abs(s[h, :, 2:12, i] - ref[:, 2:12, h])) <= 1e-5
         assert np.all(s[h, :, :2] == 0) and np.all(s[h, :, 12:] == 0)   # other blocks untouched
+
+
+# bf16, block 64, from position 0: the selection pass plus the MFMA prefill
+# attention over the per-query block sets (top-k <= 16); above that top-k the
+# same call takes one workgroup per query.
+BLOCK64_CASES = [
+    (1, 3, 64, 16, 1, 1000),    # ragged T, the largest top-k of the MFMA path
+    (2, 2, 128, 0, 0, 640),     # first and own block only; lists kept in the workspace
+    (1, 2, 128, 16, 0, 448),    # at most 5 candidates: every one kept
+    (1, 2, 64, 20, 1, 512),     # top-k above the MFMA path's limit
+]
+
+
+@pytest.mark.parametrize("case", BLOCK64_CASES, ids=["ragged-k16", "k0", "all-kept", "k20"])
+def test_topk_prefill_block64(case):
+    B, H, Dh, topk, score, T = case
+    _run(B, H, Dh, 64, topk, score, [T], 0, torch.bfloat16, seed=36)
+
+
+def test_topk_prefill_lists_in_workspace():
+    """Without a chosen buffer the selection lists live in the workspace: the
+    output is the same as with one."""
+    R = need_gpu()
+    B, H, Dh, T, block, topk = 1, 2, 128, 768, 64, 8
+    max_pos = T + block
+    x = inputs.prefill_inputs(B, T, H, Dh, dtype=torch.bfloat16, mu=1.5, seed=37)
+    d = {n: t.contiguous().to(DEV) for n, t in x.items()}
+    outs = []
+    for with_chosen in (True, False):
+        cache = R.topk_cache(B, H, Dh, max_pos, block, torch.bfloat16, DEV)
+        chosen = torch.full((B, T, H, topk), -7, dtype=torch.int32, device=DEV) if with_chosen else None
+        outs.append(R.rat_topk_prefill(d["q"], d["k"], d["v"], d["zk"], d["zv"], cache, 0, max_pos, block, topk, 1,
+                                       chosen=chosen).clone())
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_topk_prefill_full_size_sampled():
+    """T = 4096, 16 x 128, block 64, top-16 MoBA (the top-k prefill workload):
+    sampled rows against the oracle's attention over the kernel's (validated)
+    choice."""
+    R = need_gpu()
+    B, H, Dh, T, block, topk, score = 1, 16, 128, 4096, 64, 16, 1
+    max_pos = T + block
+    x = inputs.prefill_inputs(B, T, H, Dh, dtype=torch.bfloat16, mu=2.0, seed=38)
+    q = f64(x["q"])
+    Kt = oracle.scan(f64(x["k"]), f64(x["zk"]))
+    Vt = oracle.scan(f64(x["v"]), f64(x["zv"]))
+    Kr = torch.from_numpy(Kt).to(torch.bfloat16).double().numpy()
+    cache = R.topk_cache(B, H, Dh, max_pos, block, torch.bfloat16, DEV)
+    d = {n: t.contiguous().to(DEV) for n, t in x.items()}
+    chosen = torch.full((B, T, H, topk), -7, dtype=torch.int32, device=DEV)
+    out = R.rat_topk_prefill(d["q"], d["k"], d["v"], d["zk"], d["zv"], cache, 0, max_pos, block, topk, score,
+                             chosen=chosen)
+    torch.cuda.synchronize()
+    o = f64(out)
+    c = chosen.cpu().numpy()
+    rng = np.random.default_rng(39)
+    rows = [(0, int(t), int(h)) for t, h in zip(rng.integers(0, T, 256), rng.integers(0, H, 256))]
+    rows += [(0, T - 1, 0), (0, 0, 1), (0, 63, 2), (0, 64, 3)]
+    _verify([o[b, t, h] for b, t, h in rows], [c[b, t, h] for b, t, h in rows], q, Kt, Vt, rows, block, topk,
+            TK.MOBA, BF16_TOL, TK.block_stats(Kr, block), "prefill T=4096 sampled")
+
+
+def test_topk_prefill_many_candidates_sampled():
+    """More than 1024 candidate blocks (block 4, T = 4200): the selection by
+    repeated argmax; sampled rows among the last queries and a few early
+    ones against the oracle."""
+    R = need_gpu()
+    B, H, Dh, T, block, topk, score = 1, 2, 64, 4200, 4, 3, 0
+    max_pos = T + block
+    x = inputs.prefill_inputs(B, T, H, Dh, dtype=torch.bfloat16, mu=1.5, seed=40)
+    q = f64(x["q"])
+    Kt = oracle.scan(f64(x["k"]), f64(x["zk"]))
+    Vt = oracle.scan(f64(x["v"]), f64(x["zv"]))
+    Kr = torch.from_numpy(Kt).to(torch.bfloat16).double().numpy()
+    cache = R.topk_cache(B, H, Dh, max_pos, block, torch.bfloat16, DEV)
+    d = {n: t.contiguous().to(DEV) for n, t in x.items()}
+    chosen = torch.full((B, T, H, topk), -7, dtype=torch.int32, device=DEV)
+    out = R.rat_topk_prefill(d["q"], d["k"], d["v"], d["zk"], d["zv"], cache, 0, max_pos, block, topk, score,
+                             chosen=chosen)
+    torch.cuda.synchronize()
+    o = f64(out)
+    c = chosen.cpu().numpy()
+    rows = [(0, t, h) for t in (T - 1, T - 2, T - 37, 4105, 4101) for h in range(H)] + [(0, 200, 0), (0, 9, 1)]
+    _verify([o[b, t, h] for b, t, h in rows], [c[b, t, h] for b, t, h in rows], q, Kt, Vt, rows, block, topk,
+            TK.QUEST, BF16_TOL, TK.block_stats(Kr, block), "prefill T=4200 block=4")
