@@ -719,7 +719,7 @@ rat_status_t rat_topk_prefill(const void* q, const void* k, const void* v, const
   int32_t* lists = chosen ? chosen : sel;
   tp.chosen = lists;
   tp.select_only = 1;
-  e = rat::launch_topk_attend(tp, stream);
+  e = T <= rat::kTopkTileMaxT ? rat::launch_topk_select_tile(tp, stream) : rat::launch_topk_attend(tp, stream);
   if (e != hipSuccess) return fail(RAT_ERR_HIP, "top-k selection launch: %s", hipGetErrorString(e));
   rat::AttnPlan ap;
   std::memset(&ap, 0, sizeof(ap));

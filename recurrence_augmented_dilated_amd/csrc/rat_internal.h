@@ -260,6 +260,10 @@ struct TopkPlan {
 hipError_t launch_topk_stats(const TopkPlan& p, int64_t j_lo, int64_t j_hi, hipStream_t s);
 // Queries (prefill rows or one decode token per sequence): selection and attention.
 hipError_t launch_topk_attend(const TopkPlan& p, hipStream_t s);
+// Prefill selection only (chosen lists), tiles of 64 queries sharing their
+// candidates: bf16, block 64, p0 = 0, T <= kTopkTileMaxT.
+constexpr int kTopkTileMaxT = 64 * 257;
+hipError_t launch_topk_select_tile(const TopkPlan& p, hipStream_t s);
 
 struct TopkAppendPlan {
   const void* k; const void* v;      // [B][H][Dh]

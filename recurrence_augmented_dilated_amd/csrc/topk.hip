@@ -12,11 +12,14 @@
 // lower block index).
 //
 // Every recurrent state sits in a cache [H][B][max_pos][Dh]; the summaries
-// of complete blocks in fp32 [H][B][max_pos / block][3][Dh].  One workgroup
-// handles one query: it scores the candidate blocks from the summaries into
-// LDS, takes the top k by repeated wave-wide argmax, then streams the rows
-// of the kept blocks (Dh / 8 lanes per row, online softmax per lane group,
-// waves merged in LDS).
+// of complete blocks in fp32 [H][B][max_pos / block][3][Dh].  The general
+// path gives one workgroup to one query: it scores the candidate blocks from
+// the summaries into LDS, takes the top k by rank (up to 1024 candidates) or
+// by repeated wave-wide argmax, then streams the rows of the kept blocks
+// (Dh / 8 lanes per row, online softmax per lane group, waves merged in LDS).
+// Prefill with 64-position blocks from position 0 only selects here, a tile
+// of 64 queries per workgroup (they share their candidates), and attends on
+// the MFMA prefill attention kernel with the chosen lists.
 #include "rat_internal.h"
 #include "kv_stream.h"
 
@@ -119,6 +122,125 @@ __device__ __forceinline__ bool better(float v, int j, float bv, int bi) {
   return v == v && (v > bv || (v == bv && j < bi));
 }
 
+// ---- selection for a tile of 64 queries (block size 64, positions from 0):
+// the tile's queries share one block and hence one candidate set, so the
+// candidates' summaries are read once per tile.  A lane holds one query
+// (its row in registers); each wave scores every fourth candidate of a
+// 32-candidate chunk staged in LDS (broadcast reads), in fp32 like the
+// per-query kernel; then a wave per query ranks the candidates (higher
+// score, ties to the lower index) and writes the kept ones in ascending
+// order with a ballot prefix.
+constexpr int kTileQ = 64;
+constexpr int kTileChunk = 32;
+
+template <int DH>
+__global__ __launch_bounds__(kAW * 64) void topk_select_tile_kernel(const TopkPlan p, int ncap) {
+  extern __shared__ float s_tsc[];   // [kTileQ][ncap] candidate scores
+  __shared__ __attribute__((aligned(16))) float s_st[2][kTileChunk][DH];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int ntile = (p.T + kTileQ - 1) / kTileQ;
+  const int BH = p.B * p.H;
+  const int tile = ntile - 1 - int(blockIdx.x / BH);   // heaviest tiles first
+  const int bh = int(blockIdx.x % BH);
+  const int b = bh / p.H;
+  const int h = bh - b * p.H;
+  const int ncand = tile > 1 ? tile - 1 : 0;           // candidate blocks 1 .. tile-1
+  const int t = tile * kTileQ + lane;
+  const bool live = t < p.T;
+
+  // this lane's query (fp32)
+  float qv[DH];
+  {
+    const bf16_t* qp = static_cast<const bf16_t*>(p.q) + (((int64_t)b * p.T + (live ? t : 0)) * p.H + h) * DH;
+#pragma unroll
+    for (int i = 0; i < DH / 8; ++i) {
+      const uint4 w = *reinterpret_cast<const uint4*>(qp + 8 * i);
+      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        qv[8 * i + 2 * k] = bf16_lo(u[k]);
+        qv[8 * i + 2 * k + 1] = bf16_hi(u[k]);
+      }
+    }
+  }
+
+  const int64_t nbcap = p.max_pos / p.block;
+  const float* sb = p.summary + summary_off(p.B, nbcap, h, b, 0, DH);
+  const bool quest = p.score == kTopkQuest;
+  for (int c0 = 0; c0 < ncand; c0 += kTileChunk) {
+    const int nc = min(kTileChunk, ncand - c0);
+    // stage the chunk: Quest min and max, MoBA mean
+    for (int e = tid; e < nc * (DH / 4); e += kAW * 64) {
+      const int ci = e / (DH / 4), d4 = e - ci * (DH / 4);
+      const float* src = sb + (int64_t)(c0 + 1 + ci) * 3 * DH + 4 * d4;
+      if (quest) {
+        *reinterpret_cast<float4*>(&s_st[0][ci][4 * d4]) = *reinterpret_cast<const float4*>(src);
+        *reinterpret_cast<float4*>(&s_st[1][ci][4 * d4]) = *reinterpret_cast<const float4*>(src + DH);
+      } else {
+        *reinterpret_cast<float4*>(&s_st[0][ci][4 * d4]) = *reinterpret_cast<const float4*>(src + 2 * DH);
+      }
+    }
+    __syncthreads();
+    for (int ci = wave; ci < nc; ci += kAW) {
+      float sc = 0.f;
+      if (quest) {
+#pragma unroll
+        for (int d4 = 0; d4 < DH / 4; ++d4) {
+          const float4 mn = *reinterpret_cast<const float4*>(&s_st[0][ci][4 * d4]);
+          const float4 mx = *reinterpret_cast<const float4*>(&s_st[1][ci][4 * d4]);
+          sc += fmaxf(qv[4 * d4] * mn.x, qv[4 * d4] * mx.x);
+          sc += fmaxf(qv[4 * d4 + 1] * mn.y, qv[4 * d4 + 1] * mx.y);
+          sc += fmaxf(qv[4 * d4 + 2] * mn.z, qv[4 * d4 + 2] * mx.z);
+          sc += fmaxf(qv[4 * d4 + 3] * mn.w, qv[4 * d4 + 3] * mx.w);
+        }
+      } else {
+#pragma unroll
+        for (int d4 = 0; d4 < DH / 4; ++d4) {
+          const float4 me = *reinterpret_cast<const float4*>(&s_st[0][ci][4 * d4]);
+          sc = fmaf(qv[4 * d4], me.x, sc);
+          sc = fmaf(qv[4 * d4 + 1], me.y, sc);
+          sc = fmaf(qv[4 * d4 + 2], me.z, sc);
+          sc = fmaf(qv[4 * d4 + 3], me.w, sc);
+        }
+      }
+      s_tsc[lane * ncap + c0 + ci] = sc == sc ? sc : -INFINITY;
+    }
+    __syncthreads();
+  }
+
+  // a wave per query: ranks, then the kept blocks in ascending order
+  const int nsel = ncand < p.topk ? ncand : p.topk;
+  for (int qi = wave; qi < kTileQ; qi += kAW) {
+    const int tq = tile * kTileQ + qi;
+    if (tq >= p.T) break;
+    int32_t* cp = p.chosen + (((int64_t)b * p.T + tq) * p.H + h) * p.topk;
+    const float* row = s_tsc + qi * ncap;
+    int base = 0;
+    if (ncand <= p.topk) {
+      for (int j = lane; j < ncand; j += 64) cp[j] = j + 1;
+      base = ncand;
+    } else {
+      for (int j0 = 0; j0 < ncand; j0 += 64) {
+        const int j = j0 + lane;
+        const bool in = j < ncand;
+        const float v = in ? row[j] : 0.f;
+        int r = 0;
+        for (int i = 0; i < ncand; ++i) {
+          const float u = row[i];
+          r += (u > v || (u == v && i < j)) ? 1 : 0;
+        }
+        const bool kept = in && r < nsel;
+        const uint64_t m = __ballot(kept);
+        if (kept) cp[base + __builtin_popcountll(m & ((1ull << lane) - 1ull))] = j + 1;
+        base += __builtin_popcountll(m);
+      }
+    }
+    for (int j = base + lane; j < p.topk; j += 64) cp[j] = -1;
+  }
+}
+
 // Candidate counts up to this are selected by rank in one pass; larger ones
 // by repeated wave-wide argmax.
 constexpr int kRankMax = 1024;
@@ -180,7 +302,6 @@ __global__ __launch_bounds__(kAW * 64) void topk_attend_kernel(const TopkPlan p)
 #pragma unroll
     for (int i = 0; i < 8; ++i) qd[i] = s_q[8 * c + i];
     const int slot = wave * KPW + rg;                 // candidate slot of this lane group
-#pragma unroll 4
     for (int j0 = 0; j0 < ncand; j0 += kAW * KPW) {
       const int j = j0 + slot;
       const bool ok = j < ncand;
@@ -369,6 +490,16 @@ hipError_t launch_topk_append(const TopkAppendPlan& p, hipStream_t s) {
     hipLaunchKernelGGL(topk_append_kernel<bf16_t>, dim3(blocks), dim3(p.Dh), 0, s, p);
   else
     hipLaunchKernelGGL(topk_append_kernel<float>, dim3(blocks), dim3(p.Dh), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_select_tile(const TopkPlan& p, hipStream_t s) {
+  const int ntile = (p.T + kTileQ - 1) / kTileQ;
+  const int ncap = (ntile > 2 ? ntile - 2 : 0) | 1;   // candidate slots per query row (odd: no bank conflicts)
+  const size_t lds = sizeof(float) * (size_t)kTileQ * ncap;
+  const dim3 grid((unsigned)(ntile * p.B * p.H)), threads(kAW * 64);
+  if (p.Dh == 128) hipLaunchKernelGGL((topk_select_tile_kernel<128>), grid, threads, lds, s, p, ncap);
+  else hipLaunchKernelGGL((topk_select_tile_kernel<64>), grid, threads, lds, s, p, ncap);
   return hipGetLastError();
 }
 
