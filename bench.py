@@ -53,7 +53,8 @@ KERNEL_SOURCES = {"scan": ["scan.hip", "rat_internal.h"], "attention": ["prefill
                   "decode": ["decode.hip", "kv_stream.h", "rat_internal.h"],
                   "topk_attend": ["topk.hip", "kv_stream.h", "rat_internal.h"],
                   "topk_stats": ["topk.hip", "rat_internal.h"], "topk_append": ["topk.hip", "rat_internal.h"],
-                  "grid_to_col": ["chunk.hip", "rat_internal.h"], "ring_prefix": ["chunk.hip", "rat_internal.h"]}
+                  "grid_to_col": ["chunk.hip", "rat_internal.h"], "ring_prefix": ["chunk.hip", "rat_internal.h"],
+                  "topk_select": ["topk.hip", "rat_internal.h"]}
 
 
 def source_hash(kernel):
@@ -483,7 +484,7 @@ def measure_copy(torch):
 KERNEL_PATTERNS = {"scan": "scan_kernel", "attention": "attn_bf16_kernel", "decode": "decode_kernel",
                    "topk_attend": "topk_attend_kernel", "topk_stats": "topk_stats_kernel",
                    "topk_append": "topk_append_kernel", "grid_to_col": "grid_to_col_kernel",
-                   "ring_prefix": "ring_prefix_kernel"}
+                   "ring_prefix": "ring_prefix_kernel", "topk_select": "topk_select_tile_kernel"}
 COPY_BYTES = 1 << 30   # --calibrate-copy: bytes read and bytes written by one copy
 
 
