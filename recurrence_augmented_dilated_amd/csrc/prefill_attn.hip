@@ -279,6 +279,22 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
     }
   };
 
+  // per-lane byte offsets of the V^T fragments in a tile: the chunk of
+  // 16-key step st for head-dim rows 32 db + n depends on db only through its
+  // parity (rows 64 apart share the swizzle), so eight offsets serve all
+  // (st, db), the rest is an immediate
+  uint32_t vo[4][2];
+#pragma unroll
+  for (int st = 0; st < 4; ++st)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int d = 32 * p + n;
+      vo[st][p] = uint32_t(d * (kBN * 2) + 16 * ((2 * st + g) ^ col_swz(d)));
+    }
+  auto v_at = [&](const char* cV, int st, int db) __attribute__((always_inline)) -> uint4 {
+    return *reinterpret_cast<const uint4*>(cV + vo[st][db & 1] + (db >> 1) * (64 * kBN * 2));
+  };
+
   floatx16_t o[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i)
@@ -381,8 +397,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
     uint4 vpre[2 * DB];
 #pragma unroll
     for (int j = 0; j < 2 * DB; ++j) {
-      const int st = j / DB, d = 32 * (j % DB) + n;
-      vpre[j] = *reinterpret_cast<const uint4*>(cV + d * (kBN * 2) + 16 * ((2 * st + g) ^ col_swz(d)));
+      vpre[j] = v_at(cV, j / DB, j % DB);
     }
 
     // ---- online softmax (base 2; running max shared by the two lane halves)
@@ -430,10 +445,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
       const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pws[st]);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int d = 32 * db + n;
         // keys 16st + 4g + {0..3} and 16st + 8 + 4g + {0..3}: one 16-byte chunk
-        const uint4 vw = st < 2 ? vpre[st * DB + db]
-                                : *reinterpret_cast<const uint4*>(cV + d * (kBN * 2) + 16 * ((2 * st + g) ^ col_swz(d)));
+        const uint4 vw = st < 2 ? vpre[st * DB + db] : v_at(cV, st, db);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vw), pf, o[db], 0, 0, 0);
       }
     }
@@ -442,13 +455,20 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
   constexpr int LPW = KL + VL;   // direct loads per wave per tile
   constexpr int kAhead = 3;      // tiles in flight ahead of the one consumed
   floatx16_t sc[2];
-  auto tile = [&](int it) __attribute__((always_inline)) {
+  // Tile it in ring slot S (= it & 3), a compile-time constant: every LDS
+  // read then addresses a per-lane base plus an immediate offset.
+  using Slot0 = std::integral_constant<int, 0>;
+  using Slot1 = std::integral_constant<int, 1>;
+  using Slot2 = std::integral_constant<int, 2>;
+  using Slot3 = std::integral_constant<int, 3>;
+  auto tile = [&](int it, auto S) __attribute__((always_inline)) {
+    constexpr int slot = decltype(S)::value;
     bool is_grid, needed, masked;
     int kbase;
     tile_info(it, is_grid, needed, masked, kbase);
     if (needed) {
-      scores(sK[it & 3], sc);
-      finish(it, sV[it & 3], sc);
+      scores(sK[slot], sc);
+      finish(it, sV[slot], sc);
     }
   };
 
@@ -464,14 +484,20 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
       wait_vmcnt<0>();
       ring_barrier();
     }
-    for (int t0 = 0; t0 < ntiles; t0 += 2) {
-#pragma unroll
-      for (int q = 2; q < 4; ++q)
-        if (t0 + q < ntiles) issue(t0 + q, sK[(t0 + q) & 3], sV[(t0 + q) & 3]);
-      tile(t0);
-      if (t0 + 1 < ntiles) tile(t0 + 1);
+    auto pair = [&](int t0, auto SA, auto SB) __attribute__((always_inline)) {
+      constexpr int sa = decltype(SA)::value;
+      constexpr int sb = decltype(SB)::value;
+      // the next pair goes into the slots of the previous one
+      if (t0 + 2 < ntiles) issue(t0 + 2, sK[sa ^ 2], sV[sa ^ 2]);
+      if (t0 + 3 < ntiles) issue(t0 + 3, sK[sb ^ 2], sV[sb ^ 2]);
+      tile(t0, SA);
+      if (t0 + 1 < ntiles) tile(t0 + 1, SB);
       wait_vmcnt<0>();
       ring_barrier();
+    };
+    for (int t0 = 0; t0 < ntiles; t0 += 4) {
+      pair(t0, Slot0{}, Slot1{});
+      if (t0 + 2 < ntiles) pair(t0 + 2, Slot2{}, Slot3{});
     }
   } else {
     if constexpr (SEL) {
@@ -493,16 +519,24 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
       ring_barrier();
     }
     if constexpr (SEL) sel_nxt = s_sel[sel_row];
-    for (int it = 0; it < ntiles; ++it) {
-      if (it + kAhead < ntiles) issue(it + kAhead, sK[(it + kAhead) & 3], sV[(it + kAhead) & 3]);
+    auto step = [&](int it, auto S) __attribute__((always_inline)) {
+      constexpr int slot = decltype(S)::value;
+      // tile it + kAhead goes into the slot of tile it - 1
+      if (it + kAhead < ntiles) issue(it + kAhead, sK[(slot + kAhead) & 3], sV[(slot + kAhead) & 3]);
       if constexpr (SEL) sel_advance(it);
-      tile(it);
+      tile(it, S);
       // tile it+1 must have landed; later tiles may still fly
       const int later = min(ntiles - 1, it + kAhead) - (it + 1);
       if (later >= 2) wait_vmcnt<2 * LPW>();
       else if (later == 1) wait_vmcnt<LPW>();
       else wait_vmcnt<0>();
       ring_barrier();
+    };
+    for (int it = 0; it < ntiles; it += 4) {
+      step(it, Slot0{});
+      if (it + 1 < ntiles) step(it + 1, Slot1{});
+      if (it + 2 < ntiles) step(it + 2, Slot2{});
+      if (it + 3 < ntiles) step(it + 3, Slot3{});
     }
   }
 
