@@ -67,30 +67,62 @@ __global__ void states_to_ring_kernel(const RingPrefixPlan p, int64_t ring_from,
   static_cast<ET*>(p.ring_v)[dst] = vv;
 }
 
-// One thread per (b, h, d, column i < vgcap[h]): column i of row d of the
-// transposed grid values is grid entry i (zero past rows[h]).  Consecutive
-// threads take consecutive columns, so the writes are contiguous.
-__global__ void grid_to_col_kernel(const GridColPlan p, int64_t total_cols) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  // locate (h, b, d, col) from the flat index over heads in order
-  int64_t rem = i;
+// One workgroup per (h, b, 64-entry block of the grid): the block's rows
+// (16-byte loads) into a padded LDS tile, then each thread writes whole
+// 16-byte chunks of the transposed rows: physical chunk p of row d holds
+// logical chunk c = p ^ col_swz(d), i.e. entries 16 (c / 2) + 4 (c % 2) +
+// {0..3} and the four 8 further on (col_key_pos order).  Entries at or past
+// rows[h] are written as zeros (the attention reads whole 64-key tiles).
+template <int DH>
+__global__ __launch_bounds__(256) void grid_to_col_kernel(const GridColPlan p) {
+  // padded LDS row (bytes, an odd number of dwords): the eight entries a
+  // thread gathers and those of the other lanes fall in distinct banks
+  constexpr int kRow = DH * 2 + 20;
+  __shared__ __attribute__((aligned(16))) char s_t[64 * kRow];
+  // locate (h, b, block) from the flat workgroup index over heads in order
+  int64_t rem = blockIdx.x;
   int h = 0;
   for (; h < p.H; ++h) {
-    const int64_t n = (int64_t)p.B * p.Dh * p.vgcap[h];
+    const int64_t n = (int64_t)p.B * (p.vgcap[h] / 64);
     if (rem < n) break;
     rem -= n;
   }
-  if (h >= p.H || i >= total_cols) return;
+  if (h >= p.H) return;
+  const int nblk = p.vgcap[h] / 64;
+  const int b = int(rem / nblk);
+  const int jb = int(rem - (int64_t)b * nblk);
+  const int tid = threadIdx.x;
+  const int rows = p.rows[h];
+  const bf16_t* src = static_cast<const bf16_t*>(p.src) + grid_row_offset(p.heads, p.B, b, h, (int64_t)jb * 64, DH);
+  constexpr int CPR = DH / 8;   // 16-byte chunks per grid row
+#pragma unroll
+  for (int k = 0; k < 64 * CPR / 256; ++k) {
+    const int e = tid + 256 * k;
+    const int r = e / CPR, q = e - r * CPR;
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (jb * 64 + r < rows) w = *reinterpret_cast<const uint4*>(src + (int64_t)r * DH + 8 * q);
+    uint32_t* t = reinterpret_cast<uint32_t*>(s_t + r * kRow + 16 * q);   // 4-byte aligned only
+    t[0] = w.x; t[1] = w.y; t[2] = w.z; t[3] = w.w;
+  }
+  __syncthreads();
   const int cap = p.vgcap[h];
-  const int col = int(rem % cap);
-  rem /= cap;
-  const int d = int(rem % p.Dh);
-  const int b = int(rem / p.Dh);
-  bf16_t v = 0;
-  if (col < p.rows[h])
-    v = static_cast<const bf16_t*>(p.src)[grid_row_offset(p.heads, p.B, b, h, col, p.Dh) + d];
-  static_cast<bf16_t*>(p.dst)[((int64_t)p.B * p.vgoff[h] + (int64_t)b * cap) * p.Dh + (int64_t)d * cap +
-                              col_key_pos(col, d)] = v;
+  bf16_t* dst = static_cast<bf16_t*>(p.dst) + ((int64_t)p.B * p.vgoff[h] + (int64_t)b * cap) * DH + (int64_t)jb * 64;
+#pragma unroll
+  for (int k = 0; k < DH * 8 / 256; ++k) {
+    const int e = tid + 256 * k;
+    const int d = e >> 3, ph = e & 7;
+    const int c = ph ^ col_swz(d);
+    const int j0 = 16 * (c >> 1) + 4 * (c & 1);
+    const uint16_t* col = reinterpret_cast<const uint16_t*>(s_t) + d;
+    uint32_t v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = col[(j0 + i) * (kRow / 2)];
+      v[4 + i] = col[(j0 + 8 + i) * (kRow / 2)];
+    }
+    const uint4 w = make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
+    *reinterpret_cast<uint4*>(dst + (int64_t)d * cap + 8 * ph) = w;
+  }
 }
 
 }  // namespace
@@ -121,12 +153,11 @@ hipError_t launch_states_to_ring(const RingPrefixPlan& p, int64_t ring_from, hip
 }
 
 hipError_t launch_grid_to_col(const GridColPlan& p, hipStream_t s) {
-  int64_t total = 0;
-  for (int h = 0; h < p.H; ++h) total += (int64_t)p.B * p.Dh * p.vgcap[h];
-  if (total <= 0) return hipSuccess;
-  const int threads = 256;
-  const int64_t blocks = (total + threads - 1) / threads;
-  hipLaunchKernelGGL(grid_to_col_kernel, dim3((unsigned)blocks), dim3(threads), 0, s, p, total);
+  int64_t blocks = 0;
+  for (int h = 0; h < p.H; ++h) blocks += (int64_t)p.B * (p.vgcap[h] / 64);
+  if (blocks <= 0) return hipSuccess;
+  if (p.Dh == 128) hipLaunchKernelGGL(grid_to_col_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  else hipLaunchKernelGGL(grid_to_col_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
