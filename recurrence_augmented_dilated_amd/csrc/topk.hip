@@ -241,8 +241,8 @@ __global__ __launch_bounds__(kAW * 64) void topk_select_tile_kernel(const TopkPl
   }
 }
 
-// Candidate counts up to this are selected by rank in one pass; larger ones
-// by repeated wave-wide argmax.
+// Candidate counts up to this may be selected by rank in one pass (when that
+// costs less than the argmax rounds); otherwise by repeated wave-wide argmax.
 constexpr int kRankMax = 1024;
 
 // ---- selection and attention: one workgroup per query
@@ -332,9 +332,11 @@ __global__ __launch_bounds__(kAW * 64) void topk_attend_kernel(const TopkPlan p)
   const int nsel = ncand < p.topk ? ncand : p.topk;
   if (ncand <= p.topk) {
     for (int j = tid; j < ncand; j += kAW * 64) s_list[1 + j] = j + 1;
-  } else if (ncand <= kRankMax) {
-    // rank of every candidate: the number that beat it (higher score, ties
-    // to the lower index); the kept ones are the ranks below nsel
+  } else if (ncand <= kRankMax &&
+             ncand * ((ncand + kAW * 64 - 1) / (kAW * 64)) < nsel * (ncand / 64 + 12)) {
+    // rank of every candidate (cheaper than nsel argmax rounds for few
+    // candidates): the number that beat it (higher score, ties to the lower
+    // index); the kept ones are the ranks below nsel
     for (int j = tid; j < ncand; j += kAW * 64) {
       const float v = s_sc[j];
       int r = 0;
