@@ -10,8 +10,11 @@ measured in the same run and reported under "decode".  Prints one JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps N]
                     [--no-decode] [--no-cpu-baseline] [--config N]
 
---config N (1..5) measures one workload alone (auxiliary).  Inputs are
-seeded synthetic data generated on the GPU and resident in HBM before timing.
+--config N measures one workload alone: 1-3 prefill (tiny fp32, the default,
+long), 4-5 decode (batched, hybrid heads), 6 chunked prefill, 7-8 top-k
+decode and prefill, 9 RAT chunk-local prefill, 10 hybrid-head prefill.
+Inputs are seeded synthetic data generated on the GPU and resident in HBM
+before timing.
 """
 from __future__ import annotations
 
@@ -40,6 +43,9 @@ CONFIGS = {
             dtype="bf16", mu=2.0),
     8: dict(kind="topk_prefill", B=1, H=16, Dh=128, T=4096, block=64, topk=16, score=1, dtype="bf16", mu=2.0),
     9: dict(kind="local", B=1, H=16, Dh=128, T=16384, L=16, dtype="bf16", mu=2.0),
+    # prefill of the hybrid-head mix (per-head dilation, ragged compact grid)
+    10: dict(kind="prefill", B=1, H=32, Dh=128, T=16384, D=[1] * 8 + [16] * 12 + [64] * 12, W=64, dtype="bf16",
+             mu=2.0),
 }
 
 
@@ -94,11 +100,12 @@ def prefill_pairs(T, D, W):
 
 def prefill_work(c):
     B, H, Dh, T, D, W = c["B"], c["H"], c["Dh"], c["T"], c["D"], c["W"]
+    Ds = D if isinstance(D, list) else [D] * H     # dilation per head
     e = 2 if c["dtype"] == "bf16" else 4
     n = B * T * H * Dh
     scan_read = 2 * n * (e + 4)                    # x and fp32 logits, keys and values
-    scan_write = 2 * n * e if W > 0 else 2 * B * (T // D) * H * Dh * e
-    pairs = prefill_pairs(T, D, W) * B * H
+    scan_write = 2 * n * e if W > 0 else 2 * B * sum(T // d for d in Ds) * Dh * e
+    pairs = sum(prefill_pairs(T, d, W) for d in Ds) * B
     flops = 4 * Dh * pairs
     return dict(scan_bytes=scan_read + scan_write, attn_flops=flops, pairs=pairs)
 
@@ -456,7 +463,8 @@ def cpu_baseline_prefill(c, x, torch, heads):
     lim = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
     with lim:
         t0 = time.perf_counter()
-        oracle.prefill(xs["q"], xs["k"], xs["v"], xs["zk"], xs["zv"], c["D"], c["W"])
+        D = [c["D"][h] for h in hs] if isinstance(c["D"], list) else c["D"]
+        oracle.prefill(xs["q"], xs["k"], xs["v"], xs["zk"], xs["zv"], D, c["W"])
         sec = time.perf_counter() - t0
     full = sec * c["H"] / len(hs)
     tok_s = c["B"] * c["T"] / full
@@ -642,12 +650,14 @@ def main():
         }
         dom = "scan" if p["ms_scan"] >= p["ms_attn"] else "attention"
         k = kernels[dom]
-        wkey = f"prefill_T{c['T']}_D{c['D']}_W{c['W']}"
+        dname = (c["D"] if not isinstance(c["D"], list) else
+                 "x".join(f"{d}:{c['D'].count(d)}" for d in sorted(set(c["D"]))))
+        wkey = f"prefill_T{c['T']}_D{dname}_W{c['W']}"
         result.update({
             "value": tok_s, "steps": a.steps, "warmup": a.warmup, "ms_per_step": p["ms"],
             "single_call_ms_per_step": p["ms_call"],
             "dtype": c["dtype"],
-            "config": {"workload": f"prefill B={c['B']} H={c['H']} Dh={c['Dh']} T={c['T']} D={c['D']} "
+            "config": {"workload": f"prefill B={c['B']} H={c['H']} Dh={c['Dh']} T={c['T']} D={dname} "
                                    f"W={c['W']} {c['dtype']}", "config_id": cfg_id, "B": c["B"], "T": c["T"],
                        "heads": c["H"], "head_dim": c["Dh"], "dilation": c["D"], "window": c["W"]},
             "roofline": {"kernel": dom, "bound": k["bound"], "achieved": k["achieved"], "peak": k["peak"],

@@ -38,7 +38,8 @@ def _prefill_check(B, T, H, Dh, D, W, mu, seed, head_group):
     x = inputs.prefill_inputs(B, T, H, Dh, dtype=torch.bfloat16, mu=mu, seed=seed, device=DEV)
     out = R.rat_dilated_prefill(x["q"], x["k"], x["v"], x["zk"], x["zv"], D, W)
     torch.cuda.synchronize()
-    rows = _sample_rows(T, D, seed)
+    Ds = D if isinstance(D, list) else [D] * H
+    rows = sorted(set().union(*(_sample_rows(T, d, seed) for d in sorted(set(Ds)))))
     ridx = torch.tensor(rows, device=DEV)
     got = f64(out[:, ridx])
     worst = 0.0
@@ -49,7 +50,7 @@ def _prefill_check(B, T, H, Dh, D, W, mu, seed, head_group):
         Vt = oracle.scan(f64(x["v"][:, :, hs]), f64(x["zv"][:, :, hs]))
         q = np.zeros((B, T, head_group, Dh))
         q[:, rows] = f64(x["q"][:, ridx][:, :, hs])
-        ref = oracle.prefill(q, None, None, None, None, D, W, rows=rows, states=(Kt, Vt))
+        ref = oracle.prefill(q, None, None, None, None, Ds[hs], W, rows=rows, states=(Kt, Vt))
         worst = max(worst, report(f"prefill T={T} heads {h0}+", got[:, :, hs], ref[:, rows]))
         del Kt, Vt, q, ref
     return worst
@@ -58,6 +59,13 @@ def _prefill_check(B, T, H, Dh, D, W, mu, seed, head_group):
 def test_config2_prefill_full_size():
     """B=1, 16 x 128, T=16384, D=16, W=128, bf16, z ~ N(2,1)."""
     assert _prefill_check(1, 16384, 16, 128, 16, 128, 2.0, 2, head_group=16) <= BF16_TOL
+
+
+def test_hybrid_head_prefill_full_size():
+    """B=1, 32 x 128, T=16384, W=64, per-head dilation 8 x D=1, 12 x 16,
+    12 x 64 (the hybrid-head mix), bf16, z ~ N(2,1)."""
+    D = [1] * 8 + [16] * 12 + [64] * 12
+    assert _prefill_check(1, 16384, 32, 128, D, 64, 2.0, 10, head_group=8) <= BF16_TOL
 
 
 def test_config3_long_prefill_full_size():
