@@ -28,11 +28,14 @@
 // 32-bit lane offset.  Softmax runs in base 2 with the scale folded into one
 // FMA, a v_maximum3 max tree, a lazily raised running max (the O rescale is
 // rare) and row sums taken by v_dot2 over the same bf16 weights that enter
-// P V.  Block order is heaviest q-tile first and keeps each (b, h) pair on
-// one XCD.
+// P V.  Block order: dilation classes densest first, within a class the
+// heaviest q-tile first with each (b, h) pair kept on one XCD.  A dense head
+// with a window reads its grid from the all-state arrays (no second copy).
 //
 // fp32 kernel.  A plain exact-fp32 path (one or two lanes per query, keys
 // staged in LDS) for fp32 inputs.
+#include <algorithm>
+
 #include "rat_internal.h"
 
 namespace rat {
@@ -61,6 +64,12 @@ struct AttnArgs {
   int32_t vgcap[kMaxHeads];   // grid values: capacity (row length in kGridHeadCol)
   const int32_t* sel;         // block-selection mode: chosen blocks [B][T][H][sel_k]
   int sel_k;
+  // dilation classes, densest first: class c holds heads hord[cls_h0[c] ..
+  // cls_h0[c + 1]) and blocks [cls_b0[c], cls_b0[c + 1])
+  int ncls;
+  int cls_h0[kMaxCls + 1];
+  int cls_b0[kMaxCls + 1];
+  uint8_t hord[kMaxHeads];
 };
 static_assert(sizeof(AttnArgs) <= 4096, "kernel argument size");
 
@@ -89,6 +98,24 @@ __device__ __forceinline__ void block_coords(int bid, int B, int H, int n_qtiles
   qtile = n_qtiles - 1 - r;
   b = p / H;
   h = p - b * H;
+}
+
+// Block -> (b, h, q-tile) over the dilation classes: a class's blocks run
+// before those of sparser heads, so the heads whose key sets outgrow an XCD's
+// L2 have their q-tiles in flight together and stream the same keys; within a
+// class block_coords applies.  Every class but the last is padded to a
+// multiple of 8 blocks, which keeps its XCD pinning; padding blocks get false.
+__device__ __forceinline__ bool attn_block(const AttnArgs& a, int& b, int& h, int& qtile) {
+  const int bid = blockIdx.x;
+  int c = 0;
+  while (c + 1 < a.ncls && bid >= a.cls_b0[c + 1]) ++c;
+  const int nh = a.cls_h0[c + 1] - a.cls_h0[c];
+  const int rel = bid - a.cls_b0[c];
+  if (rel >= a.B * nh * a.n_qtiles) return false;
+  int hi;
+  block_coords(rel, a.B, nh, a.n_qtiles, b, hi, qtile);
+  h = a.hord[a.cls_h0[c] + hi];
+  return true;
 }
 
 
@@ -185,7 +212,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
   __shared__ __attribute__((aligned(1024))) char sV[4][VBYTES];
 
   int b, h, qtile;
-  block_coords(blockIdx.x, a.B, a.H, a.n_qtiles, b, h, qtile);
+  if (!attn_block(a, b, h, qtile)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -229,14 +256,18 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
   const int ng_w0 = wave_live ? n_grid(tw0, W, D) : 0;
   const int ng_w1 = wave_live ? n_grid(tw1, W, D) : 0;
 
-  // row length of the transposed grid values; in block-selection mode the
-  // values are kAllHeadCol rows of tpad columns
-  const int cap = SEL ? int(a.tpad) : a.vgcap[h];
-  const bf16_t* gk = static_cast<const bf16_t*>(a.grid_k) + grid_row_offset(a.heads, a.B, b, h, 0, DH);
-  const bf16_t* gvt = static_cast<const bf16_t*>(a.grid_v) +
-                      (SEL ? ((int64_t)b * H + h) * DH * a.tpad : ((int64_t)a.B * a.vgoff[h] + (int64_t)b * cap) * DH);
   const bf16_t* ak = W > 0 ? static_cast<const bf16_t*>(a.all_k) + (int64_t)b * a.arows * rowC + h * DH : nullptr;
   const bf16_t* avt = W > 0 ? static_cast<const bf16_t*>(a.all_v) + ((int64_t)b * H + h) * DH * a.tpad : nullptr;
+  // A dense head with a window may have no stored grid (capacity 0): with
+  // D = 1 and the all-state rows starting at position 0, grid entry i is
+  // all-state row i, read in the window's layouts.
+  const bool galias = !SEL && W > 0 && a.vgcap[h] == 0;
+  // row length of the transposed grid values; in block-selection mode the
+  // values are kAllHeadCol rows of tpad columns
+  const int cap = SEL || galias ? int(a.tpad) : a.vgcap[h];
+  const bf16_t* gk = galias ? ak : static_cast<const bf16_t*>(a.grid_k) + grid_row_offset(a.heads, a.B, b, h, 0, DH);
+  const bf16_t* gvt = galias ? avt : static_cast<const bf16_t*>(a.grid_v) +
+                      (SEL ? ((int64_t)b * H + h) * DH * a.tpad : ((int64_t)a.B * a.vgoff[h] + (int64_t)b * cap) * DH);
 
   // issue the direct loads of tile `it` into (dK, dV)
   // per-lane parts of the direct-load addresses (bytes): K row within the
@@ -258,7 +289,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
     v_off_g[u] = d * uint32_t(cap) * 2u + 16u * uint32_t(lane % 8);
     v_off_w[u] = W > 0 ? d * uint32_t(a.tpad) * 2u + 16u * uint32_t(lane % 8) : 0u;
   }
-  const uint32_t krow_g = DH * 2, krow_w = uint32_t(rowC) * 2u;   // K row strides (bytes)
+  const uint32_t krow_w = uint32_t(rowC) * 2u, krow_g = galias ? krow_w : DH * 2;   // K row strides (bytes)
 
   // issue the direct loads of tile `it` into (dK, dV); the tile's first row
   // goes into the wave-uniform base, rows past the last valid one re-read it
@@ -572,7 +603,7 @@ __global__ __launch_bounds__(64 * (DH / 64)) void attn_f32_kernel(const AttnArgs
   __shared__ __attribute__((aligned(16))) float sV[kF32Keys][DH];
 
   int b, h, qtile;
-  block_coords(blockIdx.x, a.B, a.H, a.n_qtiles, b, h, qtile);
+  if (!attn_block(a, b, h, qtile)) return;
   const int tid = threadIdx.x;
   const int qi = tid / TPQ;
   const int part = tid - qi * TPQ;      // which 64 head dims
@@ -668,9 +699,25 @@ __global__ __launch_bounds__(64 * (DH / 64)) void attn_f32_kernel(const AttnArgs
   }
 }
 
-int xcd_padded_blocks(int BH, int n_qtiles) {
-  if (BH % 8 == 0) return BH * n_qtiles;   // exact: npx = BH / 8 pairs per XCD
-  return BH * n_qtiles;
+// Dilation classes of the launch (heads sorted by dilation, at most kMaxCls
+// classes: the last one takes every remaining head); returns the grid size.
+int set_classes(const AttnPlan& p, AttnArgs& a) {
+  int idx[kMaxHeads];
+  for (int h = 0; h < p.H; ++h) idx[h] = h;
+  std::stable_sort(idx, idx + p.H, [&](int x, int y) { return p.heads.dil[x] < p.heads.dil[y]; });
+  a.ncls = 0;
+  for (int i = 0; i < p.H; ++i) {
+    a.hord[i] = (uint8_t)idx[i];
+    if (i == 0 || (p.heads.dil[idx[i]] != p.heads.dil[idx[i - 1]] && a.ncls < kMaxCls))
+      a.cls_h0[a.ncls++] = i;
+  }
+  a.cls_h0[a.ncls] = p.H;
+  a.cls_b0[0] = 0;
+  for (int c = 0; c < a.ncls; ++c) {
+    const int n = p.B * (a.cls_h0[c + 1] - a.cls_h0[c]) * a.n_qtiles;
+    a.cls_b0[c + 1] = a.cls_b0[c] + (c + 1 < a.ncls ? (n + 7) / 8 * 8 : n);
+  }
+  return a.cls_b0[a.ncls];
 }
 
 }  // namespace
@@ -694,10 +741,9 @@ hipError_t launch_prefill_attention(const AttnPlan& p, hipStream_t s) {
     a.vgoff[h] = p.vgoff[h];
     a.vgcap[h] = p.vgcap[h];
   }
-  const int BH = p.B * p.H;
   if (p.bf16) {
     a.n_qtiles = (p.T + kBM - 1) / kBM;
-    const int blocks = xcd_padded_blocks(BH, a.n_qtiles);
+    const int blocks = set_classes(p, a);
     if (p.sel) {
       if (p.Dh == 128)
         hipLaunchKernelGGL((attn_bf16_kernel<128, true>), dim3(blocks), dim3(kWaves * 64), 0, s, a);
@@ -710,7 +756,7 @@ hipError_t launch_prefill_attention(const AttnPlan& p, hipStream_t s) {
     }
   } else {
     a.n_qtiles = (p.T + 63) / 64;
-    const int blocks = xcd_padded_blocks(BH, a.n_qtiles);
+    const int blocks = set_classes(p, a);
     if (p.Dh == 128)
       hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(blocks), dim3(128), 0, s, a);
     else

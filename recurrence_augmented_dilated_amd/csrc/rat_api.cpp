@@ -63,14 +63,17 @@ rat_status_t check_dilation(const int32_t* dilation, int32_t H) {
 // sequence; the bf16 path pads every head's capacity to a multiple of 64
 // keys (whole attention tiles) and keeps values transposed (kGridHeadCol),
 // keys row-major (kGridHeadRow); the fp32 path keeps both row-major.
-void prefill_grid_layout(int32_t T, int32_t H, const int32_t* dilation, bool bf16,
+// With bf16 and a window, a dense head (D = 1) stores no grid: its grid
+// entries are the all-state rows, which the attention reads in their place
+// (capacity 0 marks such a head).
+void prefill_grid_layout(int32_t T, int32_t H, const int32_t* dilation, bool bf16, int32_t W,
                          rat::HeadTable& ht, int64_t& rows) {
   rows = 0;
   std::memset(&ht, 0, sizeof(ht));
   for (int h = 0; h < H; ++h) {
     const int32_t G = T / dilation[h];
     ht.dil[h] = dilation[h];
-    ht.gcap[h] = bf16 ? (G + 63) / 64 * 64 : G;
+    ht.gcap[h] = bf16 && W > 0 && dilation[h] == 1 ? 0 : bf16 ? (G + 63) / 64 * 64 : G;
     ht.goff[h] = rows;
     rows += ht.gcap[h];
   }
@@ -87,7 +90,7 @@ PrefillCarve prefill_carve(int32_t B, int32_t T, int32_t H, int32_t Dh, const in
   rat::HeadTable ht;
   int64_t rows;
   const bool bf16 = dt == RAT_BF16;
-  prefill_grid_layout(T, H, dilation, bf16, ht, rows);
+  prefill_grid_layout(T, H, dilation, bf16, W, ht, rows);
   PrefillCarve c;
   c.scan_bytes = align_up(rat::scan_workspace_bytes(2, B, T, H, Dh));
   c.grid_bytes = align_up((size_t)B * rows * Dh * elt_size(dt));
@@ -275,7 +278,7 @@ rat_status_t rat_dilated_prefill_stage(rat_prefill_stage_t stage, const void* q,
   rat::ScanPlan sp;
   std::memset(&sp, 0, sizeof(sp));
   int64_t rows;
-  prefill_grid_layout(T, H, dilation, bf16, sp.heads, rows);
+  prefill_grid_layout(T, H, dilation, bf16, W, sp.heads, rows);
   sp.ten[0] = {k, zk, nullptr, all_k, grid_k, nullptr, rat::kAllToken, rat::kGridHeadRow};
   sp.ten[1] = {v, zv, nullptr, all_v, grid_v, nullptr, bf16 ? rat::kAllHeadCol : rat::kAllToken,
                bf16 ? rat::kGridHeadCol : rat::kGridHeadRow};

@@ -8,6 +8,7 @@
 namespace rat {
 
 constexpr int kMaxHeads = 128;
+constexpr int kMaxCls = 8;   // dilation classes the attention launch orders its blocks by
 
 // ---------------------------------------------------------------------------
 // bf16 helpers (storage is raw uint16_t; arithmetic is fp32)

@@ -361,7 +361,10 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
   int64_t grid_i = (next_grid_abs + 1) / D - 1;
 
   XT* out_all = static_cast<XT*>(tn.out_all);
-  XT* out_grid = static_cast<XT*>(tn.out_grid);
+  // a head with no stored grid (capacity 0 in a per-head layout) reads its
+  // grid entries from the all-state outputs instead
+  XT* out_grid = tn.grid_mode != kGridToken && a.heads.gcap[h] == 0 ? nullptr
+                                                                   : static_cast<XT*>(tn.out_grid);
   const int64_t G_tok = T / D;
   const bool tok_all = out_all && tn.all_mode == kAllToken;
   const bool col_all = out_all && tn.all_mode == kAllHeadCol;

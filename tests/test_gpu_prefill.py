@@ -65,6 +65,18 @@ def test_per_head_dilation():
     assert err <= BF16_TOL
 
 
+def test_many_dilation_classes():
+    """24 heads over 13 distinct dilations: the launch orders blocks by class
+    (at most 8 classes, the last one merges the sparsest), pads classes to 8
+    blocks, keeps the 16 dense (b, h) pairs XCD-pinned, and the dense heads read
+    their grid from the all-state arrays."""
+    dil = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 1, 1, 16, 2, 64, 3, 1, 5, 9, 700, 1, 1, 1, 1]
+    x = inputs.prefill_inputs(2, 600, 24, 64, dtype=torch.bfloat16, seed=31)
+    out = _gpu(x, dil, 12)
+    err = report("13 dilation classes", f64(out), _ref(x, dil, 12))
+    assert err <= BF16_TOL
+
+
 def _onehot_inputs(T, H, Dh, dtype, hot, seed):
     """Gates closed (z = -inf: states equal raw k, v) and one key per head made
     dominant: queries that see position `hot` return v[hot] almost exactly,
@@ -85,7 +97,8 @@ def _onehot_inputs(T, H, Dh, dtype, hot, seed):
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
 @pytest.mark.parametrize("D,W,hot", [(4, 0, 63), (4, 0, 64), (4, 0, 67), (16, 8, 47), (16, 8, 95),
-                                     (16, 8, 96), (3, 5, 100), (8, 0, 7), (1, 0, 128)])
+                                     (16, 8, 96), (3, 5, 100), (8, 0, 7), (1, 0, 128), (1, 8, 100),
+                                     (1, 8, 200), (1, 70, 130)])
 def test_key_set_boundaries_onehot(dtype, D, W, hot):
     T, H, Dh = 256, 2, 128
     x = _onehot_inputs(T, H, Dh, dtype, hot, seed=hot)
