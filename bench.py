@@ -145,6 +145,17 @@ def time_loop(fn, steps, torch):
     return e0.elapsed_time(e1) / steps
 
 
+def inputs_sha256(x, torch):
+    """SHA-256 over the bytes of q, k, v, zk, zv in that order (host copies,
+    taken after the timed region)."""
+    import hashlib
+    h = hashlib.sha256()
+    for key in ("q", "k", "v", "zk", "zv"):
+        t = x[key].contiguous()
+        h.update(t.view(torch.uint8).cpu().numpy().tobytes())
+    return h.hexdigest()
+
+
 def bench_prefill(c, steps, warmup, torch, R, inputs):
     dev = "cuda:0"
     dt = torch.bfloat16 if c["dtype"] == "bf16" else torch.float32
@@ -192,7 +203,7 @@ def bench_prefill(c, steps, warmup, torch, R, inputs):
     log(f"[bench] prefill {ms:.3f} ms/step (wall {wall:.3f}; single call {ms_call:.3f}); "
         f"scan {ms_scan:.3f} ms, attention {ms_attn:.3f} ms per launch; ws error {err}")
     return dict(ms=ms, ms_call=ms_call, wall_ms=wall, ms_scan=ms_scan, ms_attn=ms_attn, x=x, out=out,
-                ws_error=err)
+                ws_error=err, inputs_sha256=inputs_sha256(x, torch))
 
 
 def bench_decode(c, steps, warmup, torch, R, inputs):
@@ -450,7 +461,9 @@ def aux_result(cfg_id, c, a, torch, R, inputs):
 
 def cpu_baseline_prefill(c, x, torch, heads):
     """The fp64 oracle on `heads` of the workload's heads (every query row, the
-    full-length recurrence), one thread; tokens/s scaled by H / len(heads)."""
+    full-length recurrence), one thread; tokens/s scaled by H / len(heads).
+    With a per-head dilation list the sample is one head per dilation, each
+    time scaled by the number of heads with that dilation."""
     import contextlib
     import oracle
     try:
@@ -458,19 +471,32 @@ def cpu_baseline_prefill(c, x, torch, heads):
     except ImportError:  # pragma: no cover
         threadpool_limits = None
     f = lambda t: t.float().cpu().double().numpy()  # noqa: E731
-    hs = list(range(heads))
-    xs = {k: f(v[:, :, hs]) for k, v in x.items()}
+    if isinstance(c["D"], list):
+        groups = [([h for h in range(c["H"]) if c["D"][h] == d][:1], c["D"].count(d), d)
+                  for d in sorted(set(c["D"]))]
+    else:
+        # at most ~2e8 (query, key) pairs of oracle work, at least one head
+        per_head = max(1, prefill_pairs(c["T"], c["D"], c["W"]) * c["B"])
+        heads = max(1, min(heads, c["H"], int(2e8 // per_head)))
+        groups = [(list(range(heads)), c["H"], c["D"])]
     lim = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
+    sec = full = 0.0
     with lim:
-        t0 = time.perf_counter()
-        D = [c["D"][h] for h in hs] if isinstance(c["D"], list) else c["D"]
-        oracle.prefill(xs["q"], xs["k"], xs["v"], xs["zk"], xs["zv"], D, c["W"])
-        sec = time.perf_counter() - t0
-    full = sec * c["H"] / len(hs)
+        for hs, count, d in groups:
+            xs = {k: f(v[:, :, hs]) for k, v in x.items()}
+            t0 = time.perf_counter()
+            oracle.prefill(xs["q"], xs["k"], xs["v"], xs["zk"], xs["zv"], d, c["W"])
+            dt = time.perf_counter() - t0
+            log(f"[bench] cpu baseline: D={d}, {len(hs)} head(s): {dt:.1f} s")
+            sec += dt
+            full += dt * count / len(hs)
     tok_s = c["B"] * c["T"] / full
+    n = sum(len(g[0]) for g in groups)
+    how = ("one head per dilation, each scaled by its head count" if isinstance(c["D"], list)
+           else f"tokens/s scaled by H/{n}")
     return dict(value=tok_s, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"fp64 oracle prefill of {len(hs)} of {c['H']} heads (all {c['T']} query rows and the "
-                       f"full recurrence) took {sec:.1f} s on 1 thread; tokens/s scaled by H/{len(hs)}")
+                sample=f"fp64 oracle prefill of {n} of {c['H']} heads (all {c['T']} query rows and the "
+                       f"full recurrence) took {sec:.1f} s on 1 thread; {how}")
 
 
 def measure_copy(torch):
@@ -650,9 +676,10 @@ def main():
         }
         dom = "scan" if p["ms_scan"] >= p["ms_attn"] else "attention"
         k = kernels[dom]
+        # a per-head dilation list is named by its (dilation x heads) groups
         dname = (c["D"] if not isinstance(c["D"], list) else
-                 "x".join(f"{d}:{c['D'].count(d)}" for d in sorted(set(c["D"]))))
-        wkey = f"prefill_T{c['T']}_D{dname}_W{c['W']}"
+                 ",".join(f"{d}x{c['D'].count(d)}" for d in sorted(set(c["D"]))))
+        wkey = f"prefill_T{c['T']}_D{str(dname).replace(',', '-')}_W{c['W']}"
         result.update({
             "value": tok_s, "steps": a.steps, "warmup": a.warmup, "ms_per_step": p["ms"],
             "single_call_ms_per_step": p["ms_call"],
@@ -664,6 +691,7 @@ def main():
                          "unit": k["unit"], "frac": k["frac"], "traffic": measured_traffic(dom, wkey)},
             "kernels": kernels,
             "ws_error": p["ws_error"],
+            "inputs_sha256": p["inputs_sha256"],
             "copy_GBps_measured": measure_copy(torch),
         })
         for name in kernels:

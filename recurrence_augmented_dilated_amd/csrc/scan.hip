@@ -369,6 +369,15 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
   const bool tok_all = out_all && tn.all_mode == kAllToken;
   const bool col_all = out_all && tn.all_mode == kAllHeadCol;
   const bool col_grid = out_grid && tn.grid_mode == kGridHeadCol;
+  // A dense head's transposed grid (D = 1, entry i at position i, chunks
+  // 64-aligned) takes the LDS-staged 16-byte stores of the all-state output;
+  // stage_grid (block-uniform) says whether any head of the slab does so.
+  bool stage_grid = false;
+  if (sizeof(XT) == 2 && tn.out_grid && tn.grid_mode == kGridHeadCol && (a.p0 & 63) == 0) {
+    for (int hh = cs * SC / a.Dh; hh <= (cs * SC + SC - 1) / a.Dh; ++hh)
+      stage_grid |= a.heads.dil[hh] == 1 && a.heads.gcap[hh] > 0 && (a.heads.gcap[hh] & 63) == 0;
+  }
+  const bool dense_col = stage_grid && col_grid && D == 1 && (a.heads.gcap[h] & 63) == 0;
   // per-channel row bases of the column layouts
   const int64_t col_all_row = (((int64_t)b * a.H + h) * a.Dh + d) * a.tpad;
   const int64_t col_grid_row = col_grid ? grid_row_offset(a.heads, a.B, b, h, 0, a.Dh) +
@@ -396,7 +405,7 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
           V::store(out_grid + (((int64_t)b * G_tok + i) * a.H + h) * a.Dh + d, hv);
         } else if (tn.grid_mode == kGridHeadRow) {
           V::store(out_grid + grid_row_offset(a.heads, a.B, b, h, i, a.Dh) + d, hv);
-        } else {
+        } else if (!dense_col) {
 #pragma unroll
           for (int c = 0; c < NC; ++c)
             store1(out_grid + col_grid_row + (int64_t)c * a.heads.gcap[h] + col_key_pos(i, d + c), hv[c]);
@@ -408,7 +417,7 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
         for (int c = 0; c < NC; ++c) tn.h_last[((int64_t)b * a.H + h) * a.Dh + d + c] = hv[c];
       }
     }
-    if (col_all) {
+    if (col_all || dense_col) {
       // keys t-3..t of each channel; positions past T are written as zeros
 #pragma unroll
       for (int c = 0; c < NC; ++c) run[c][s & 3] = t < T ? hv[c] : 0.f;
@@ -427,13 +436,14 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
     }
   }
   if constexpr (sizeof(XT) == 2) {
-    if (col_all) {
+    if (col_all || stage_grid) {
       // Write the chunk's [channel][128 keys] block into the transposed rows
       // with 16-byte stores.  In col_key_pos order the physical 8-key chunk p
       // of a 64-key tile holds logical chunk c = p ^ col_swz(d): keys
       // 16(c/2) + 4(c%2) + {0..3} and the four keys 8 further on.
       __syncthreads();
       const int64_t key0 = a.all_row0 + (int64_t)chunk * kChunkT;   // a multiple of 64
+      const int64_t gkey0 = a.p0 + (int64_t)chunk * kChunkT;       // dense grid entry of step 0
       constexpr int CPR = kChunkT / 8;   // 16-byte chunks per channel row
 #pragma unroll
       for (int k = 0; k < SC * CPR / (kNW * 64); ++k) {
@@ -449,8 +459,13 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
         const uint2 w1 = *reinterpret_cast<const uint2*>(s_T + r * kTRow + 2 * (k0 + 8));
         const uint4 w = make_uint4(w0.x, w0.y, w1.x, w1.y);
         const int64_t kpos = key0 + p * 8;
-        if (kpos < a.tpad)
+        if (col_all && kpos < a.tpad)
           *reinterpret_cast<uint4*>(out_all + (((int64_t)b * a.H + hh) * a.Dh + dd) * a.tpad + kpos) = w;
+        const int gc = a.heads.gcap[hh];
+        const int64_t gpos = gkey0 + p * 8;
+        if (stage_grid && a.heads.dil[hh] == 1 && gc > 0 && (gc & 63) == 0 && gpos < gc)
+          *reinterpret_cast<uint4*>(static_cast<XT*>(tn.out_grid) + grid_row_offset(a.heads, a.B, b, hh, 0, a.Dh) +
+                                    (int64_t)dd * gc + gpos) = w;
       }
     }
   }

@@ -65,15 +65,18 @@ def test_per_head_dilation():
     assert err <= BF16_TOL
 
 
-def test_many_dilation_classes():
+@pytest.mark.parametrize("W", [12, 0])
+def test_many_dilation_classes(W):
     """24 heads over 13 distinct dilations: the launch orders blocks by class
     (at most 8 classes, the last one merges the sparsest), pads classes to 8
-    blocks, keeps the 16 dense (b, h) pairs XCD-pinned, and the dense heads read
-    their grid from the all-state arrays."""
+    blocks and keeps the 16 dense (b, h) pairs XCD-pinned.  With a window the
+    dense heads read their grid from the all-state arrays; without one the
+    scan writes their transposed grid through LDS, next to a sparser head in
+    the same 128-channel slab (Dh = 64)."""
     dil = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 1, 1, 16, 2, 64, 3, 1, 5, 9, 700, 1, 1, 1, 1]
-    x = inputs.prefill_inputs(2, 600, 24, 64, dtype=torch.bfloat16, seed=31)
-    out = _gpu(x, dil, 12)
-    err = report("13 dilation classes", f64(out), _ref(x, dil, 12))
+    x = inputs.prefill_inputs(2, 600, 24, 64, dtype=torch.bfloat16, seed=31 + W)
+    out = _gpu(x, dil, W)
+    err = report(f"13 dilation classes W={W}", f64(out), _ref(x, dil, W))
     assert err <= BF16_TOL
 
 
