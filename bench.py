@@ -145,17 +145,6 @@ def time_loop(fn, steps, torch):
     return e0.elapsed_time(e1) / steps
 
 
-def inputs_sha256(x, torch):
-    """SHA-256 over the bytes of q, k, v, zk, zv in that order (host copies,
-    taken after the timed region)."""
-    import hashlib
-    h = hashlib.sha256()
-    for key in ("q", "k", "v", "zk", "zv"):
-        t = x[key].contiguous()
-        h.update(t.view(torch.uint8).cpu().numpy().tobytes())
-    return h.hexdigest()
-
-
 def bench_prefill(c, steps, warmup, torch, R, inputs):
     dev = "cuda:0"
     dt = torch.bfloat16 if c["dtype"] == "bf16" else torch.float32
@@ -203,7 +192,7 @@ def bench_prefill(c, steps, warmup, torch, R, inputs):
     log(f"[bench] prefill {ms:.3f} ms/step (wall {wall:.3f}; single call {ms_call:.3f}); "
         f"scan {ms_scan:.3f} ms, attention {ms_attn:.3f} ms per launch; ws error {err}")
     return dict(ms=ms, ms_call=ms_call, wall_ms=wall, ms_scan=ms_scan, ms_attn=ms_attn, x=x, out=out,
-                ws_error=err, inputs_sha256=inputs_sha256(x, torch))
+                ws_error=err, inputs_sha256=inputs.sha256_of(x["q"], x["k"], x["v"], x["zk"], x["zv"]))
 
 
 def bench_decode(c, steps, warmup, torch, R, inputs):
@@ -311,15 +300,9 @@ def bench_topk_decode(c, steps, warmup, torch, R):
     max_pos = ctx + max(steps, warmup) + blk
     max_pos = (max_pos + blk - 1) // blk * blk
     cache = R.topk_cache(B, H, Dh, max_pos, blk, torch.bfloat16, dev)
-    g = torch.Generator(device=dev).manual_seed(7)
-    for name in ("cache_k", "cache_v"):
-        buf = cache[name]
-        for h in range(H):
-            buf[h].copy_(torch.randn(buf[h].shape, generator=g, device=dev).to(torch.bfloat16))
-    cache["state_k"].normal_(generator=g)
-    cache["state_v"].normal_(generator=g)
-    R.rat_topk_summarize(cache, 0, ctx // blk, max_pos, blk)
     from recurrence_augmented_dilated_amd import inputs
+    inputs.fill_topk_cache(cache, seed=7)
+    R.rat_topk_summarize(cache, 0, ctx // blk, max_pos, blk)
     n_in = max(steps, warmup)
     st = inputs.decode_step_inputs(B, H, Dh, n_in, mu=c["mu"], seed=5, device=dev)
     pos = torch.full((B,), ctx, dtype=torch.int32, device=dev)

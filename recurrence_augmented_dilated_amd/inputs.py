@@ -6,7 +6,8 @@ fp64 oracle (through the tests) take their inputs from here.
 
 Recipe: q, k, v ~ N(0, 1), drawn in fp32 and cast to the compute dtype with
 round-to-nearest-even; gate logits z ~ N(mu, 1) in fp32 (one set for keys,
-one for values); decode caches (fp32 state, bf16 grid and ring) ~ N(0, 1).
+one for values); decode caches (fp32 state, bf16 grid and ring) and top-k
+state caches ~ N(0, 1).
 Draw order is fixed: q, k, v, zk, zv, then caches, then per-step inputs.
 """
 from __future__ import annotations
@@ -88,6 +89,21 @@ def decode_cache(B, H, Dh, dilation, W, context, steps, dtype=torch.bfloat16, se
             buf[s:e] = _normal((e - s,), g, device).to(dtype)
     return dict(state_k=state_k, state_v=state_v, ring_k=ring_k, ring_v=ring_v,
                 grid_k=grid_k, grid_v=grid_v, layout=lay)
+
+
+def fill_topk_cache(cache, seed=7):
+    """Fill the state caches of a top-k cache dict (cache_k, cache_v [H, B,
+    max_pos, Dh]; state_k, state_v [B, H, Dh] fp32) with N(0, 1) values:
+    cache_k head by head, then cache_v, then state_k, state_v.  Summaries are
+    left alone (the caller computes them)."""
+    device = cache["cache_k"].device
+    g = _gen(seed, device)
+    for name in ("cache_k", "cache_v"):
+        buf = cache[name]
+        for h in range(buf.shape[0]):
+            buf[h].copy_(torch.randn(buf[h].shape, generator=g, device=device).to(buf.dtype))
+    cache["state_k"].normal_(generator=g)
+    cache["state_v"].normal_(generator=g)
 
 
 def decode_step_inputs(B, H, Dh, steps, dtype=torch.bfloat16, mu=2.0, seed=0, device="cpu"):
