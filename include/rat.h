@@ -110,7 +110,10 @@ rat_status_t rat_scan(const void* x, const float* z, const float* h0, void* stat
  *   ws        workspace of at least rat_dilated_prefill_workspace_size(...)
  *             bytes; it receives the recurrent states
  * The recurrence starts from zero state.  T = 0 is a no-op (buffers may
- * then be NULL).
+ * then be NULL).  bf16 sequences are limited to 2^31 / Dh positions
+ * (16777216 for Dh = 128): the attention addresses the transposed value rows
+ * with 32-bit offsets; longer ones -> RAT_ERR_UNSUPPORTED before anything
+ * runs.
  * ------------------------------------------------------------------------ */
 size_t rat_dilated_prefill_workspace_size(int32_t B, int32_t T, int32_t H, int32_t Dh,
                                           const int32_t* dilation, int32_t W,
@@ -179,7 +182,9 @@ rat_status_t rat_grid_layout(int32_t H, const int32_t* dilation, int64_t max_pos
  *                bytes (scratch only: nothing in it is read by a later call)
  * Errors: p0 not a multiple of 64 -> RAT_ERR_UNSUPPORTED; p0 < 0,
  * p0 + T > max_pos or a grid capacity below max_pos / D_h ->
- * RAT_ERR_INVALID_ARG.  T = 0 is a no-op (buffers may then be NULL).
+ * RAT_ERR_INVALID_ARG; bf16 with the chunk's window rows or a head's visible
+ * grid above 2^31 / Dh keys -> RAT_ERR_UNSUPPORTED (as rat_dilated_prefill).
+ * T = 0 is a no-op (buffers may then be NULL).
  * ------------------------------------------------------------------------ */
 size_t rat_prefill_chunk_workspace_size(int32_t B, int32_t T, int32_t H, int32_t Dh,
                                         const int32_t* dilation, int32_t W, int64_t p0,
@@ -294,7 +299,8 @@ typedef enum { RAT_TOPK_QUEST = 0, RAT_TOPK_MOBA = 1 } rat_topk_score_t;
  * block = 64, topk <= 16 and p0 = 0 select first and then run the MFMA
  * prefill attention over the cache with the per-query block sets (the
  * workspace then also holds the transposed values and the chosen lists);
- * other calls take one workgroup per query. */
+ * other calls, and sequences past 2^31 / Dh positions, take one workgroup
+ * per query. */
 size_t rat_topk_prefill_workspace_size(int32_t B, int32_t T, int32_t H, int32_t Dh);
 rat_status_t rat_topk_prefill(const void* q, const void* k, const void* v, const float* zk,
                               const float* zv, void* out, int32_t* chosen, float* state_k,

@@ -724,6 +724,13 @@ int set_classes(const AttnPlan& p, AttnArgs& a) {
 
 hipError_t launch_prefill_attention(const AttnPlan& p, hipStream_t s) {
   if (p.T <= 0 || p.B <= 0) return hipSuccess;
+  if (p.bf16) {
+    // 32-bit per-lane byte offsets into the transposed value rows
+    const int64_t lim = (int64_t(1) << 31) / p.Dh;
+    bool ok = p.tpad <= lim;
+    for (int h = 0; h < p.H; ++h) ok = ok && p.vgcap[h] <= lim;
+    if (!ok) return hipErrorInvalidValue;
+  }
   AttnArgs a;
   a.q = p.q; a.out = p.out;
   a.grid_k = p.grid_k; a.grid_v = p.grid_v;

@@ -52,6 +52,15 @@ rat_status_t check_ptr(const void* p, const char* name, bool nullable) {
   return RAT_OK;
 }
 
+// The bf16 attention addresses a transposed value row of `cols` keys with
+// 32-bit per-lane byte offsets: cols * Dh * 2 bytes must stay within 2^32.
+rat_status_t check_col_span(int64_t cols, int32_t Dh) {
+  if (cols * Dh > (int64_t(1) << 31))
+    return fail(RAT_ERR_UNSUPPORTED, "bf16 attention over %lld key positions with Dh %d exceeds its limit of 2^31 / Dh",
+                (long long)cols, Dh);
+  return RAT_OK;
+}
+
 rat_status_t check_dilation(const int32_t* dilation, int32_t H) {
   if (!dilation) return fail(RAT_ERR_INVALID_ARG, "dilation must not be NULL");
   for (int h = 0; h < H; ++h)
@@ -264,6 +273,7 @@ rat_status_t rat_dilated_prefill_stage(rat_prefill_stage_t stage, const void* q,
   const char* names[] = {"q", "k", "v", "zk", "zv", "out", "ws"};
   for (int i = 0; i < 7; ++i)
     if ((st = check_ptr(ptrs[i], names[i], false)) != RAT_OK) return st;
+  if (dt == RAT_BF16 && (st = check_col_span(prefill_tpad(T), Dh)) != RAT_OK) return st;
   const PrefillCarve cv = prefill_carve(B, T, H, Dh, dilation, W, dt);
   if (ws_bytes < cv.total) return fail(RAT_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, cv.total);
   if (T == 0) return ok();
@@ -364,6 +374,11 @@ static rat_status_t prefill_chunk_impl(const void* q, const void* k, const void*
   if (ws_bytes < cv.total) return fail(RAT_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, cv.total);
 
   const bool bf16 = dt == RAT_BF16;
+  if (bf16) {
+    int64_t span = cv.tpad;
+    for (int h = 0; h < H; ++h) span = std::max<int64_t>(span, cv.vgcap[h]);
+    if ((st = check_col_span(span, Dh)) != RAT_OK) return st;
+  }
   char* wb = static_cast<char*>(ws);
   float* h0k = reinterpret_cast<float*>(wb + cv.scan_bytes);
   float* h0v = h0k + (size_t)B * H * Dh;
@@ -674,9 +689,10 @@ rat_status_t rat_topk_prefill(const void* q, const void* k, const void* v, const
   // then the MFMA prefill attention runs over the dense cache with the key
   // set block 0 + chosen + own block (64-position blocks = its key tiles).
   // It needs the values transposed (written by the scan alongside the cache)
-  // and so starts at position 0; other calls take one workgroup per query.
-  const bool fast = bf16 && block == 64 && topk <= rat::kSelMaxK && p0 == 0;
+  // and so starts at position 0; other calls take one workgroup per query
+  // (as do sequences past the MFMA kernel's 2^31 / Dh positions).
   const int64_t tpad = (T + 63) / 64 * 64;
+  const bool fast = bf16 && block == 64 && topk <= rat::kSelMaxK && p0 == 0 && tpad * Dh <= (int64_t(1) << 31);
   char* vcol = reinterpret_cast<char*>(h0k) + align_up(2 * sbytes);
   int32_t* sel = reinterpret_cast<int32_t*>(vcol + align_up((size_t)B * H * Dh * tpad * 2));
   hipError_t e = hipMemcpyAsync(h0k, state_k, sbytes, hipMemcpyDeviceToDevice, stream);

@@ -69,6 +69,18 @@ def test_prefill_validation(kw, code):
     assert _prefill(**kw) == code
 
 
+def test_prefill_length_limit():
+    """bf16 attention addresses value rows with 32-bit offsets: at most
+    2^31 / Dh positions (rejected before anything is launched; at the limit
+    the call gets as far as the workspace check).  fp32 has no such limit."""
+    assert _prefill(T=1 << 24) == -3
+    assert _prefill(T=(1 << 24) + 1) == -2
+    assert b"2^31" in R.lib().rat_last_error()
+    assert _prefill(T=1 << 25, Dh=64) == -3
+    assert _prefill(T=(1 << 25) + 1, Dh=64) == -2
+    assert _prefill(T=(1 << 24) + 1, dt=0) == -3
+
+
 def test_stage_validation():
     d = (ctypes.c_int32 * 2)(4, 4)
     st = R.lib().rat_dilated_prefill_stage(9, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 2, 128, d, 0,
@@ -135,6 +147,8 @@ def test_prefill_chunk_validation():
     assert call(W=-1) == -1
     assert call() == -3                      # workspace too small
     assert call(T=0, q=None, ring=None) == 0  # empty chunk: no-op, NULL buffers allowed
+    big_cap = (ctypes.c_int32 * H)(1 << 23, 1 << 21)
+    assert call(p0=0, T=(1 << 24) + 1, max_pos=1 << 25, cap=big_cap, wsb=1 << 62) == -2   # bf16 length limit
 
 
 def test_prefill_chunk_workspace_size():
