@@ -69,7 +69,7 @@ struct AttnArgs {
   int ncls;
   int cls_h0[kMaxCls + 1];
   int cls_b0[kMaxCls + 1];
-  uint8_t hord[kMaxHeads];
+  alignas(4) uint8_t hord[kMaxHeads];
 };
 static_assert(sizeof(AttnArgs) <= 4096, "kernel argument size");
 
@@ -114,7 +114,9 @@ __device__ __forceinline__ bool attn_block(const AttnArgs& a, int& b, int& h, in
   if (rel >= a.B * nh * a.n_qtiles) return false;
   int hi;
   block_coords(rel, a.B, nh, a.n_qtiles, b, hi, qtile);
-  h = a.hord[a.cls_h0[c] + hi];
+  // the byte of hord, read as its (scalar-loadable) dword
+  const int i = a.cls_h0[c] + hi;
+  h = int((reinterpret_cast<const uint32_t*>(a.hord)[i >> 2] >> (8 * (i & 3))) & 0xffu);
   return true;
 }
 
@@ -571,22 +573,39 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
     }
   }
 
-  // ---- normalise and store (empty key set -> zeros)
+  // ---- normalise and store (empty key set -> zeros).  Every loop path
+  // ends with its loads waited for and a ring barrier, so the K ring is idle:
+  // each wave stages its 32 output rows in its own part of it (row-major,
+  // 16-byte chunks XOR-swizzled by row) and writes whole rows with 16-byte
+  // stores, one instruction covering 64 / (DH / 8) complete rows.
   float l_lo, l_hi;
   half_pair(l_run, l_lo, l_hi);
   const float l_tot = l_lo + l_hi;
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (q_live) {
-    bf16_t* op = static_cast<bf16_t*>(a.out) + ((int64_t)b * T + tq) * rowC + h * DH;
+  constexpr int CPR = DH / 8;     // 16-byte chunks per output row
+  constexpr int RPI = 64 / CPR;   // rows per store instruction
+  static_assert(kWaves * 32 * DH * 2 == 4 * KBYTES, "the output rows fill the K ring");
+  char* ep = &sK[0][0] + wave * (32 * DH * 2);
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
-        const int d = 32 * db + 8 * k4 + 4 * g;
-        const uint2 w = make_uint2(pack_bf16x2(o[db][4 * k4 + 0] * inv, o[db][4 * k4 + 1] * inv),
-                                   pack_bf16x2(o[db][4 * k4 + 2] * inv, o[db][4 * k4 + 3] * inv));
-        *reinterpret_cast<uint2*>(op + d) = w;
-      }
+    for (int k4 = 0; k4 < 4; ++k4) {
+      const int c = 4 * db + k4;   // chunk of head dims 32 db + 8 k4 .. +7; this lane's half is g
+      const uint2 w = make_uint2(pack_bf16x2(o[db][4 * k4 + 0] * inv, o[db][4 * k4 + 1] * inv),
+                                 pack_bf16x2(o[db][4 * k4 + 2] * inv, o[db][4 * k4 + 3] * inv));
+      *reinterpret_cast<uint2*>(ep + n * (DH * 2) + ((c ^ (n & (CPR - 1))) << 4) + 8 * g) = w;
+    }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's rows are in LDS
+  asm volatile("" ::: "memory");
+  bf16_t* ob = static_cast<bf16_t*>(a.out) + ((int64_t)b * T + t0 + wave * 32) * rowC + h * DH;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / CPR;   // row of the wave's 32
+    const int p = lane % CPR;             // physical chunk
+    const uint4 w = *reinterpret_cast<const uint4*>(ep + r * (DH * 2) + (p << 4));
+    if (t0 + wave * 32 + r < T)
+      *reinterpret_cast<uint4*>(ob + (int64_t)r * rowC + ((p ^ (r & (CPR - 1))) << 3)) = w;
   }
 }
 
