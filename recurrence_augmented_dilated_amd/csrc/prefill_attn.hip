@@ -31,6 +31,7 @@
 // P V.  Block order: dilation classes densest first, within a class the
 // heaviest q-tile first with each (b, h) pair kept on one XCD.  A dense head
 // with a window reads its grid from the all-state arrays (no second copy).
+// The output rows go through the idle K ring and out as whole rows.
 //
 // fp32 kernel.  A plain exact-fp32 path (one or two lanes per query, keys
 // staged in LDS) for fp32 inputs.
