@@ -12,13 +12,21 @@
 namespace rat {
 namespace {
 
-// One thread per (b, h, d, r): all-state row r < n_pre (absolute position
-// base + r) of channel d takes ring slot (base + r) % W if the position is
-// at or after ring_lo (the oldest position the ring still holds), else 0.
+// The first 2 n_state threads copy the carried states (keys, then values);
+// then one thread per (b, h, d, r): all-state row r < n_pre (absolute
+// position base + r) of channel d takes ring slot (base + r) % W if the
+// position is at or after ring_lo (the oldest position the ring still
+// holds), else 0.
 template <typename ET>
 __global__ void ring_prefix_kernel(const RingPrefixPlan p) {
   const int64_t total = (int64_t)p.B * p.H * p.n_pre * p.Dh;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < 2 * p.n_state) {
+    if (i < p.n_state) p.h0_k[i] = p.st_k[i];
+    else p.h0_v[i - p.n_state] = p.st_v[i - p.n_state];
+    return;
+  }
+  i -= 2 * p.n_state;
   if (i >= total) return;
   const int d = int(i % p.Dh);
   int64_t rest = i / p.Dh;
@@ -42,12 +50,12 @@ __global__ void ring_prefix_kernel(const RingPrefixPlan p) {
   }
 }
 
-// One thread per (b, h, d, r) for the rows r of positions ring_from + r:
-// ring slot (ring_from + r) % W <- all-state row ring_from - base + r.
+// One element (b, h, d, r), i = ((b * H + h) * n + r) * Dh + d, of the rows
+// r of positions ring_from + r: ring slot (ring_from + r) % W <- all-state
+// row ring_from - base + r.
 template <typename ET>
-__global__ void states_to_ring_kernel(const RingPrefixPlan p, int64_t ring_from, int64_t n) {
+__device__ __forceinline__ void ring_update_elem(const RingPrefixPlan& p, int64_t ring_from, int64_t n, int64_t i) {
   const int64_t total = (int64_t)p.B * p.H * n * p.Dh;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= total) return;
   const int d = int(i % p.Dh);
   int64_t rest = i / p.Dh;
@@ -65,6 +73,11 @@ __global__ void states_to_ring_kernel(const RingPrefixPlan p, int64_t ring_from,
   const int64_t dst = (((int64_t)b * p.H + h) * p.W + j % p.W) * p.Dh + d;
   static_cast<ET*>(p.ring_k)[dst] = kv;
   static_cast<ET*>(p.ring_v)[dst] = vv;
+}
+
+template <typename ET>
+__global__ void states_to_ring_kernel(const RingPrefixPlan p, int64_t ring_from, int64_t n) {
+  ring_update_elem<ET>(p, ring_from, n, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
 // One workgroup per (h, b, 64-entry block of the grid): the block's rows
@@ -87,7 +100,10 @@ __global__ __launch_bounds__(256) void grid_to_col_kernel(const GridColPlan p) {
     if (rem < n) break;
     rem -= n;
   }
-  if (h >= p.H) return;
+  if (h >= p.H) {   // past the grid: the ring update folded into this launch
+    if (p.ring_n > 0) ring_update_elem<bf16_t>(p.ring, p.ring_from, p.ring_n, rem * 256 + threadIdx.x);
+    return;
+  }
   const int nblk = p.vgcap[h] / 64;
   const int b = int(rem / nblk);
   const int jb = int(rem - (int64_t)b * nblk);
@@ -128,7 +144,7 @@ __global__ __launch_bounds__(256) void grid_to_col_kernel(const GridColPlan p) {
 }  // namespace
 
 hipError_t launch_ring_prefix(const RingPrefixPlan& p, hipStream_t s) {
-  const int64_t total = (int64_t)p.B * p.H * p.n_pre * p.Dh;
+  const int64_t total = (int64_t)p.B * p.H * p.n_pre * p.Dh + 2 * p.n_state;
   if (total <= 0) return hipSuccess;
   const int threads = 256;
   const int64_t blocks = (total + threads - 1) / threads;
@@ -155,6 +171,7 @@ hipError_t launch_states_to_ring(const RingPrefixPlan& p, int64_t ring_from, hip
 hipError_t launch_grid_to_col(const GridColPlan& p, hipStream_t s) {
   int64_t blocks = 0;
   for (int h = 0; h < p.H; ++h) blocks += (int64_t)p.B * (p.vgcap[h] / 64);
+  if (p.ring_n > 0) blocks += ((int64_t)p.B * p.H * p.ring_n * p.Dh + 255) / 256;
   if (blocks <= 0) return hipSuccess;
   if (p.Dh == 128) hipLaunchKernelGGL(grid_to_col_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, s, p);
   else hipLaunchKernelGGL(grid_to_col_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, s, p);

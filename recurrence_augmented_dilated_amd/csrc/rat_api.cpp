@@ -394,24 +394,25 @@ static rat_status_t prefill_chunk_impl(const void* q, const void* k, const void*
     cache.goff[h] = grid_off[h];
   }
 
-  // 1. the carried states: the scan reads them as h0 and writes h_last over them
-  const size_t sbytes = (size_t)B * H * Dh * sizeof(float);
-  hipError_t e = hipMemcpyAsync(h0k, state_k, sbytes, hipMemcpyDeviceToDevice, stream);
-  if (e == hipSuccess) e = hipMemcpyAsync(h0v, state_v, sbytes, hipMemcpyDeviceToDevice, stream);
-  if (e != hipSuccess) return fail(RAT_ERR_HIP, "state copy: %s", hipGetErrorString(e));
-
-  // 2. window states before p0, from the ring
-  if (W > 0 && cv.all_row0 > 0) {
+  // 1. the carried states (the scan reads them as h0 from the workspace and
+  // writes h_last over state_k / state_v) and 2. the window states before
+  // p0, from the ring: one launch
+  hipError_t e;
+  {
     rat::RingPrefixPlan rp;
-    rp.ring_k = ring_k; rp.ring_v = ring_v;
-    rp.all_k = all_k; rp.all_v = all_v;
     rp.B = B; rp.H = H; rp.Dh = Dh; rp.W = W;
-    rp.base = cv.base; rp.n_pre = cv.all_row0;
-    rp.ring_lo = std::max<int64_t>(0, p0 - W + 1);
-    rp.arows = cv.arows; rp.tpad = cv.tpad;
-    rp.bf16 = bf16;
+    rp.st_k = state_k; rp.st_v = state_v; rp.h0_k = h0k; rp.h0_v = h0v;
+    rp.n_state = (int64_t)B * H * Dh;
+    if (W > 0 && cv.all_row0 > 0) {
+      rp.ring_k = ring_k; rp.ring_v = ring_v;
+      rp.all_k = all_k; rp.all_v = all_v;
+      rp.base = cv.base; rp.n_pre = cv.all_row0;
+      rp.ring_lo = std::max<int64_t>(0, p0 - W + 1);
+      rp.arows = cv.arows; rp.tpad = cv.tpad;
+      rp.bf16 = bf16;
+    }
     e = rat::launch_ring_prefix(rp, stream);
-    if (e != hipSuccess) return fail(RAT_ERR_HIP, "ring prefix launch: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return fail(RAT_ERR_HIP, "state copy / ring prefix launch: %s", hipGetErrorString(e));
   }
 
   // 3. the recurrence from the carried states: chunk states, new grid
@@ -433,17 +434,24 @@ static rat_status_t prefill_chunk_impl(const void* q, const void* k, const void*
   sp.fallback_spins = scan_fallback_spins();
   e = rat::launch_scan(sp, stream);
   if (e != hipSuccess) return fail(RAT_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
-  if (W > 0) {   // the chunk's last min(W, T) states into the ring
-    rat::RingPrefixPlan rp;
-    rp.ring_k = ring_k; rp.ring_v = ring_v;
-    rp.all_k = all_k; rp.all_v = all_v;
-    rp.B = B; rp.H = H; rp.Dh = Dh; rp.W = W;
-    rp.base = cv.base; rp.n_pre = cv.all_row0;
-    rp.ring_lo = 0;
-    rp.arows = cv.arows; rp.tpad = cv.tpad;
-    rp.bf16 = bf16;
-    e = rat::launch_states_to_ring(rp, std::max<int64_t>(p0, p0 + T - W), stream);
-    if (e != hipSuccess) return fail(RAT_ERR_HIP, "ring update launch: %s", hipGetErrorString(e));
+  // the chunk's last min(W, T) states into the ring: a launch of its own for
+  // fp32, folded into the grid transpose's launch below for bf16
+  rat::RingPrefixPlan rr;
+  int64_t ring_from = 0, ring_n = 0;
+  if (W > 0) {
+    rr.ring_k = ring_k; rr.ring_v = ring_v;
+    rr.all_k = all_k; rr.all_v = all_v;
+    rr.B = B; rr.H = H; rr.Dh = Dh; rr.W = W;
+    rr.base = cv.base; rr.n_pre = cv.all_row0;
+    rr.ring_lo = 0;
+    rr.arows = cv.arows; rr.tpad = cv.tpad;
+    rr.bf16 = bf16;
+    ring_from = std::max<int64_t>(p0, p0 + T - W);
+    ring_n = std::max<int64_t>(0, cv.base + cv.arows - ring_from);
+    if (!bf16) {
+      e = rat::launch_states_to_ring(rr, ring_from, stream);
+      if (e != hipSuccess) return fail(RAT_ERR_HIP, "ring update launch: %s", hipGetErrorString(e));
+    }
   }
 
   // 4. bf16: the grid values the chunk's queries see, transposed
@@ -462,8 +470,11 @@ static rat_status_t prefill_chunk_impl(const void* q, const void* k, const void*
       ap.vgoff[h] = cv.vgoff[h];
       ap.vgcap[h] = cv.vgcap[h];
     }
+    gp.ring = rr;
+    gp.ring_from = ring_from;
+    gp.ring_n = ring_n;
     e = rat::launch_grid_to_col(gp, stream);
-    if (e != hipSuccess) return fail(RAT_ERR_HIP, "grid transpose launch: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return fail(RAT_ERR_HIP, "grid transpose / ring update launch: %s", hipGetErrorString(e));
   } else {
     for (int h = 0; h < H; ++h) {
       ap.vgoff[h] = grid_off[h];
@@ -695,8 +706,12 @@ rat_status_t rat_topk_prefill(const void* q, const void* k, const void* v, const
   const bool fast = bf16 && block == 64 && topk <= rat::kSelMaxK && p0 == 0 && tpad * Dh <= (int64_t(1) << 31);
   char* vcol = reinterpret_cast<char*>(h0k) + align_up(2 * sbytes);
   int32_t* sel = reinterpret_cast<int32_t*>(vcol + align_up((size_t)B * H * Dh * tpad * 2));
-  hipError_t e = hipMemcpyAsync(h0k, state_k, sbytes, hipMemcpyDeviceToDevice, stream);
-  if (e == hipSuccess) e = hipMemcpyAsync(h0v, state_v, sbytes, hipMemcpyDeviceToDevice, stream);
+  // the carried states into the workspace (the scan reads h0 there and writes
+  // h_last over state_k / state_v), one small launch for both
+  rat::RingPrefixPlan cp;
+  cp.st_k = state_k; cp.st_v = state_v; cp.h0_k = h0k; cp.h0_v = h0v;
+  cp.n_state = (int64_t)B * H * Dh;
+  hipError_t e = rat::launch_ring_prefix(cp, stream);
   if (e != hipSuccess) return fail(RAT_ERR_HIP, "state copy: %s", hipGetErrorString(e));
 
   // recurrence: every state of positions p0 .. p0+T-1 into the caches

@@ -182,11 +182,16 @@ hipError_t launch_prefill_attention(const AttnPlan& p, hipStream_t s);
 // ring slot (base + r) % W where base + r >= ring_lo, zeros elsewhere.  K in
 // kAllToken with arows rows; V in kAllHeadCol (bf16) or kAllToken (fp32).
 struct RingPrefixPlan {
-  void* ring_k; void* ring_v;               // [B][H][W][Dh]
-  void* all_k; void* all_v;
-  int B, H, Dh, W;
-  int64_t base, n_pre, ring_lo, arows, tpad;
-  int bf16;
+  void* ring_k = nullptr; void* ring_v = nullptr;   // [B][H][W][Dh]
+  void* all_k = nullptr; void* all_v = nullptr;
+  int B = 0, H = 0, Dh = 0, W = 0;
+  int64_t base = 0, n_pre = 0, ring_lo = 0, arows = 0, tpad = 0;
+  int bf16 = 0;
+  // launch_ring_prefix only: fp32 [B][H][Dh] states copied st_* -> h0_* in
+  // the same launch (n_state = B * H * Dh elements each; 0: none)
+  const float* st_k = nullptr; const float* st_v = nullptr;
+  float* h0_k = nullptr; float* h0_v = nullptr;
+  int64_t n_state = 0;
 };
 hipError_t launch_ring_prefix(const RingPrefixPlan& p, hipStream_t s);
 // The reverse: ring slots of positions [ring_from, base + arows) from the
@@ -203,6 +208,10 @@ struct GridColPlan {
   int64_t vgoff[kMaxHeads];
   int32_t vgcap[kMaxHeads];
   int32_t rows[kMaxHeads];
+  // optional, bf16: the ring update of launch_states_to_ring (positions
+  // ring_from .. ring_from + ring_n - 1) in the same launch (ring_n 0: none)
+  RingPrefixPlan ring;
+  int64_t ring_from, ring_n;
 };
 hipError_t launch_grid_to_col(const GridColPlan& p, hipStream_t s);
 
