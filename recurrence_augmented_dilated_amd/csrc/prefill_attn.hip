@@ -233,15 +233,38 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
   const bool q_live = tq < T;
   const int tqa = P0 + tq;                // its absolute position
 
-  // Q^T fragments (B operand): query tq, head dims 16*ks + 8*g .. +7
+  // Q^T fragments (B operand): query tq, head dims 16*ks + 8*g .. +7.  The
+  // wave's 32 query rows are loaded as whole rows (64 / (DH / 8) rows per
+  // instruction) into its part of the still idle K ring, 16-byte chunks
+  // XOR-swizzled by row, and read back in fragment order; a barrier then
+  // frees the ring for the first tiles.
   bf16x8_t qf[KS];
   {
-    const bf16_t* qp = static_cast<const bf16_t*>(a.q) + ((int64_t)b * T + tq) * rowC + h * DH;
+    constexpr int CPR = DH / 8;     // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;   // rows per load instruction
+    char* qs = &sK[0][0] + wave * (32 * DH * 2);
+    const bf16_t* qb = static_cast<const bf16_t*>(a.q) + (int64_t)b * T * rowC + h * DH + 8 * (lane % CPR);
+    // rows past T read row T-1 (all loads in flight at once) and store zeros
+    uint4 wq[32 / RPI];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 w = q_live ? *reinterpret_cast<const uint4*>(qp + 16 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
-      qf[ks] = __builtin_bit_cast(bf16x8_t, w);
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int row = t0 + wave * 32 + i * RPI + lane / CPR;
+      wq[i] = *reinterpret_cast<const uint4*>(qb + (int64_t)min(row, T - 1) * rowC);
     }
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = i * RPI + lane / CPR, p = lane % CPR;
+      const uint4 w = t0 + wave * 32 + r < T ? wq[i] : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(qs + r * (DH * 2) + ((p ^ (r & (CPR - 1))) << 4)) = w;
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's rows are in LDS
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
+                                                 qs + n * (DH * 2) + (((2 * ks + g) ^ (n & (CPR - 1))) << 4)));
+    ring_barrier();   // every wave has its fragments before the ring is filled
   }
 
   // key ranges of the block (window tiles start on a 64-key boundary)
