@@ -41,6 +41,7 @@ constexpr int kLW = 16;              // time steps per wave
 constexpr int kNW = 8;               // waves per block
 constexpr int kChunkT = kLW * kNW;   // time steps per block
 constexpr int kWin = 2;              // predecessors read per look-back round trip
+constexpr int kSparseMaxD = 32;      // largest D whose column grid is staged through LDS
 constexpr uint32_t kFallbackSpins = 256;   // default polls before computing a predecessor locally
 
 // Hide a register value from the optimiser (an empty asm that "modifies"
@@ -378,6 +379,18 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
       stage_grid |= a.heads.dil[hh] == 1 && a.heads.gcap[hh] > 0 && (a.heads.gcap[hh] & 63) == 0;
   }
   const bool dense_col = stage_grid && col_grid && D == 1 && (a.heads.gcap[h] & 63) == 0;
+  // A head with 2 <= D <= kSparseMaxD (a chunk holds 128 / D >= 4 of its
+  // grid entries) takes them from the same staging after the chunk: a
+  // (channel, 4-entry group) task stores four entries that are contiguous in
+  // col_key_pos order as one 8-byte piece, or at the chunk's edges its own
+  // entries one by one, instead of 2-byte stores to 64 rows per instruction.
+  // stage_sparse (block-uniform): some head of the slab does so.
+  bool stage_sparse = false;
+  if (sizeof(XT) == 2 && tn.out_grid && tn.grid_mode == kGridHeadCol) {
+    for (int hh = cs * SC / a.Dh; hh <= (cs * SC + SC - 1) / a.Dh; ++hh)
+      stage_sparse |= a.heads.dil[hh] > 1 && a.heads.dil[hh] <= kSparseMaxD && a.heads.gcap[hh] > 0;
+  }
+  const bool sparse_col = stage_sparse && col_grid && D > 1 && D <= kSparseMaxD;
   // per-channel row bases of the column layouts
   const int64_t col_all_row = (((int64_t)b * a.H + h) * a.Dh + d) * a.tpad;
   const int64_t col_grid_row = col_grid ? grid_row_offset(a.heads, a.B, b, h, 0, a.Dh) +
@@ -405,7 +418,7 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
           V::store(out_grid + (((int64_t)b * G_tok + i) * a.H + h) * a.Dh + d, hv);
         } else if (tn.grid_mode == kGridHeadRow) {
           V::store(out_grid + grid_row_offset(a.heads, a.B, b, h, i, a.Dh) + d, hv);
-        } else if (!dense_col) {
+        } else if (!dense_col && !sparse_col) {
 #pragma unroll
           for (int c = 0; c < NC; ++c)
             store1(out_grid + col_grid_row + (int64_t)c * a.heads.gcap[h] + col_key_pos(i, d + c), hv[c]);
@@ -417,7 +430,7 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
         for (int c = 0; c < NC; ++c) tn.h_last[((int64_t)b * a.H + h) * a.Dh + d + c] = hv[c];
       }
     }
-    if (col_all || dense_col) {
+    if (col_all || dense_col || sparse_col) {
       // keys t-3..t of each channel; positions past T are written as zeros
 #pragma unroll
       for (int c = 0; c < NC; ++c) run[c][s & 3] = t < T ? hv[c] : 0.f;
@@ -436,7 +449,7 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
     }
   }
   if constexpr (sizeof(XT) == 2) {
-    if (col_all || stage_grid) {
+    if (col_all || stage_grid || stage_sparse) {
       // Write the chunk's [channel][128 keys] block into the transposed rows
       // with 16-byte stores.  In col_key_pos order the physical 8-key chunk p
       // of a 64-key tile holds logical chunk c = p ^ col_swz(d): keys
@@ -466,6 +479,53 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
         if (stage_grid && a.heads.dil[hh] == 1 && gc > 0 && (gc & 63) == 0 && gpos < gc)
           *reinterpret_cast<uint4*>(static_cast<XT*>(tn.out_grid) + grid_row_offset(a.heads, a.B, b, hh, 0, a.Dh) +
                                     (int64_t)dd * gc + gpos) = w;
+      }
+      if (stage_sparse) {
+        // grid entries i whose positions (i + 1) D - 1 lie in the chunk's
+        // [pa, pb): i in [ia, ib), in groups of four from ia rounded down;
+        // per head of the slab (one or two: Dh is 64 or 128) its first entry,
+        // group count and D, then one task per (group, channel)
+        const int pa = int(a.p0) + chunk * kChunkT;
+        const int pb = int(a.p0) + min((chunk + 1) * kChunkT, T);
+        const int dsh = 31 - __builtin_clz(a.Dh);        // log2(Dh)
+        const int h_lo = (cs * SC) >> dsh;
+        int ia2[2], nq2[2], dg2[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int hh = h_lo + j;
+          const bool in = hh <= ((cs * SC + SC - 1) >> dsh);
+          const int Dg = in ? a.heads.dil[hh] : 0;
+          const bool use = in && Dg > 1 && Dg <= kSparseMaxD && a.heads.gcap[hh] > 0;
+          const int ia = use ? (pa + Dg) / Dg - 1 : 0, ib = use ? (pb + Dg) / Dg - 1 : 0;
+          ia2[j] = ia;
+          nq2[j] = use && ib > ia ? ((ib - 1) >> 2) - (ia >> 2) + 1 : 0;
+          dg2[j] = Dg;
+        }
+        const int G = max(nq2[0], nq2[1]);
+        for (int task = tid; task < SC * G; task += kNW * 64) {
+          const int q = task / SC, r = task - q * SC;     // SC is a power of two
+          const int chg = cs * SC + r;
+          const int j = (chg >> dsh) - h_lo;
+          const int dd = chg & (a.Dh - 1);
+          const int Dg = j ? dg2[1] : dg2[0];
+          const int ia = j ? ia2[1] : ia2[0];
+          if (q >= (j ? nq2[1] : nq2[0])) continue;
+          const int ib = (pb + Dg) / Dg - 1;
+          const int g0 = (ia & ~3) + 4 * q;
+          const int hh = h_lo + j;
+          const int gc = a.heads.gcap[hh];
+          const uint16_t* row = reinterpret_cast<const uint16_t*>(s_T + r * kTRow);
+          uint16_t* dst = reinterpret_cast<uint16_t*>(static_cast<XT*>(tn.out_grid) +
+                                                      grid_row_offset(a.heads, a.B, b, hh, 0, a.Dh) + (int64_t)dd * gc);
+          if (g0 >= ia && g0 + 4 <= ib) {
+            uint32_t v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = row[(g0 + e + 1) * Dg - 1 - pa];
+            *reinterpret_cast<uint2*>(dst + col_key_pos(g0, dd)) = make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
+          } else {
+            for (int i = max(g0, ia); i < min(g0 + 4, ib); ++i) dst[col_key_pos(i, dd)] = row[(i + 1) * Dg - 1 - pa];
+          }
+        }
       }
     }
   }
