@@ -118,12 +118,18 @@ def test_scan_lookback_recompute_path(dtype, monkeypatch):
     assert np.max(np.abs(f64(h_last) - ref[:, -1])) <= 1e-5
 
 
-def test_prefill_with_lookback_recompute_path(monkeypatch):
+@pytest.mark.parametrize("dil,W", [(16, 32), (16, 0), ([1, 3, 32, 33], 0), ([2, 16, 1, 64], 8)],
+                         ids=["D16-W32", "D16-W0", "mixed-W0", "mixed-W8"])
+def test_prefill_with_lookback_recompute_path(dil, W, monkeypatch):
+    """The recompute fallback on every wait, with the grid layouts the scan
+    writes from its LDS staging (dense heads, 2 <= D <= 32) and directly
+    (D > 32), with and without a window."""
     R = need_gpu()
     monkeypatch.setenv("RAT_SCAN_FALLBACK_SPINS", "0")
-    x = inputs.prefill_inputs(1, 2000, 2, 128, dtype=torch.bfloat16, seed=42)
+    H = len(dil) if isinstance(dil, list) else 2
+    x = inputs.prefill_inputs(1, 2000, H, 128, dtype=torch.bfloat16, seed=42)
     d = {k: v.to("cuda:0") for k, v in x.items()}
-    out = R.rat_dilated_prefill(d["q"], d["k"], d["v"], d["zk"], d["zv"], 16, 32)
+    out = R.rat_dilated_prefill(d["q"], d["k"], d["v"], d["zk"], d["zv"], dil, W)
     torch.cuda.synchronize()
-    ref = oracle.prefill(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["zk"]), f64(x["zv"]), 16, 32)
-    assert report("prefill fallback", f64(out), ref) <= 2e-2
+    ref = oracle.prefill(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["zk"]), f64(x["zv"]), dil, W)
+    assert report(f"prefill fallback D={dil} W={W}", f64(out), ref) <= 2e-2
