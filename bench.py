@@ -619,8 +619,8 @@ def main():
         summarize_trace(*a.summarize_trace, a.pmc_bench_args)
         return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how the operator would shard).", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(a sequence or batch split over GPUs would add carry and grid exchanges; none is built).", file=sys.stderr)
         sys.exit(2)
 
     import torch
