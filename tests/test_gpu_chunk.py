@@ -114,3 +114,28 @@ def test_chunk_equals_one_shot_prefill():
     torch.cuda.synchronize()
     err = report("chunks vs one call", f64(torch.cat(outs, dim=1)), f64(one))
     assert err <= BF16_TOL
+
+
+def _random_case(seed):
+    rng = np.random.default_rng(3000 + seed)
+    B = int(rng.integers(1, 3))
+    H = int(rng.integers(1, 5))
+    Dh = int(rng.choice([64, 128]))
+    dil = [int(rng.choice([1, 2, 3, 4, 16, 33, 64, 100])) for _ in range(H)]
+    W = int(rng.choice([0, 1, 7, 64, 130]))
+    n = int(rng.integers(1, 4))
+    chunks = [64 * int(rng.integers(1, 6)) for _ in range(n - 1)] + [int(rng.integers(1, 400))]
+    dtype = torch.float32 if rng.random() < 0.3 else torch.bfloat16
+    steps = int(rng.integers(1, 40))
+    return B, H, Dh, dil, W, chunks, dtype, steps
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_chunked_prefill_random(seed):
+    """Seeded random chunk splits, head mixes, windows and dtypes: chunk
+    outputs, caches and the decode steps that follow against the oracle."""
+    B, H, Dh, dil, W, chunks, dtype, steps = _random_case(seed)
+    print(f"[chunk-random] seed={seed} B={B} H={H} Dh={Dh} D={dil} W={W} chunks={chunks} {dtype} decode={steps}",
+          flush=True)
+    worst, tol = _run(B, H, Dh, dil, W, chunks, dtype, steps, seed=4000 + seed)
+    assert worst <= tol
