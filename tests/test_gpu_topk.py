@@ -273,3 +273,26 @@ def test_topk_prefill_many_candidates_sampled():
     rows = [(0, t, h) for t in (T - 1, T - 2, T - 37, 4105, 4101) for h in range(H)] + [(0, 200, 0), (0, 9, 1)]
     _verify([o[b, t, h] for b, t, h in rows], [c[b, t, h] for b, t, h in rows], q, Kt, Vt, rows, block, topk,
             TK.QUEST, BF16_TOL, TK.block_stats(Kr, block), "prefill T=4200 block=4")
+
+
+def _random_case(seed):
+    rng = np.random.default_rng(5000 + seed)
+    B = int(rng.integers(1, 3))
+    H = int(rng.integers(1, 4))
+    Dh = int(rng.choice([64, 128]))
+    block = int(rng.choice([16, 32, 64]))
+    topk = int(rng.choice([0, 1, 4, 16, 20]))
+    score = int(rng.integers(0, 2))
+    n = int(rng.integers(1, 3))
+    chunks = [int(rng.integers(1, 700)) for _ in range(n)]
+    steps = int(rng.integers(0, 20))
+    dtype = torch.float32 if rng.random() < 0.25 else torch.bfloat16
+    return B, H, Dh, block, topk, score, chunks, steps, dtype
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_topk_random(seed):
+    """Seeded random block sizes, budgets, scores, chunkings and dtypes
+    (including the block-64 MFMA path when the draw allows it)."""
+    B, H, Dh, block, topk, score, chunks, steps, dtype = _random_case(seed)
+    _run(B, H, Dh, block, topk, score, chunks, steps, dtype, seed=6000 + seed)
