@@ -150,3 +150,23 @@ def test_decode_bad_position_flags_error():
     assert torch.all(out[1] == 0)
     assert torch.equal(c["state_k"][1], sk0[1])
     assert not torch.equal(c["state_k"][0], sk0[0])
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_decode_random(seed):
+    """Seeded random batch, heads, head size, dilation mix, window, per-sequence
+    start positions (so the sequences of one step sit at different positions)
+    and dtype: every step against the oracle's replay."""
+    rng = np.random.default_rng(7000 + seed)
+    B = int(rng.integers(1, 5))
+    H = int(rng.integers(1, 5))
+    Dh = int(rng.choice([64, 128]))
+    dil = [int(rng.choice([1, 2, 3, 4, 16, 33, 64, 100])) for _ in range(H)]
+    W = int(rng.choice([0, 1, 7, 64]))
+    pos0 = [int(rng.integers(0, 1500)) for _ in range(B)]
+    steps = int(rng.integers(1, 30))
+    dtype = torch.float32 if rng.random() < 0.3 else torch.bfloat16
+    print(f"[decode-random] seed={seed} B={B} H={H} Dh={Dh} D={dil} W={W} pos0={pos0} steps={steps} {dtype}",
+          flush=True)
+    worst, *_ = _decode_run(B, H, Dh, dil, W, pos0, steps, dtype, seed=8000 + seed)
+    assert worst <= (F32_TOL if dtype == torch.float32 else BF16_TOL)
