@@ -634,22 +634,27 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
 }
 
 // ---------------------------------------------------------------------------
-// fp32 kernel: exact fp32 arithmetic, TPQ = DH / 64 lanes per query
+// fp32 kernel: exact fp32 arithmetic.  A block takes 64 queries; each query's
+// head dims are split over TPQ = DH / 8 lanes (8 dims per lane), so a block
+// has 8 (Dh = 64) or 16 (Dh = 128) waves and the per-key dot products are
+// short and independent (reduced over the TPQ lanes by shuffles)
 // ---------------------------------------------------------------------------
 constexpr int kF32Keys = 32;
+constexpr int kF32Dims = 8;    // head dims per lane
 
 template <int DH>
-__global__ __launch_bounds__(64 * (DH / 64)) void attn_f32_kernel(const AttnArgs a) {
-  constexpr int TPQ = DH / 64;
+__global__ __launch_bounds__(64 * (DH / kF32Dims)) void attn_f32_kernel(const AttnArgs a) {
+  constexpr int TPQ = DH / kF32Dims;
   constexpr int NT = 64 * TPQ;
   __shared__ __attribute__((aligned(16))) float sK[kF32Keys][DH];
   __shared__ __attribute__((aligned(16))) float sV[kF32Keys][DH];
+  __shared__ float sS[kF32Keys][64];   // each query's scores of the current tile
 
   int b, h, qtile;
   if (!attn_block(a, b, h, qtile)) return;
   const int tid = threadIdx.x;
   const int qi = tid / TPQ;
-  const int part = tid - qi * TPQ;      // which 64 head dims
+  const int d0 = (tid - qi * TPQ) * kF32Dims;   // this lane's first head dim
   const int T = a.T, H = a.H, W = a.W;
   const int D = a.heads.dil[h];
   const int64_t rowC = (int64_t)H * DH;
@@ -660,16 +665,16 @@ __global__ __launch_bounds__(64 * (DH / 64)) void attn_f32_kernel(const AttnArgs
   const bool q_live = tq < T;
   const int tqa = P0 + tq;
 
-  float q[64], acc[64];
+  float q[kF32Dims], acc[kF32Dims];
   {
-    const float* qp = static_cast<const float*>(a.q) + ((int64_t)b * T + tq) * rowC + h * DH + 64 * part;
+    const float* qp = static_cast<const float*>(a.q) + ((int64_t)b * T + tq) * rowC + h * DH + d0;
 #pragma unroll
-    for (int i = 0; i < 64; i += 4) {
+    for (int i = 0; i < kF32Dims; i += 4) {
       float4 w = q_live ? *reinterpret_cast<const float4*>(qp + i) : make_float4(0.f, 0.f, 0.f, 0.f);
       q[i] = w.x; q[i + 1] = w.y; q[i + 2] = w.z; q[i + 3] = w.w;
     }
 #pragma unroll
-    for (int i = 0; i < 64; ++i) acc[i] = 0.f;
+    for (int i = 0; i < kF32Dims; ++i) acc[i] = 0.f;
   }
   const int ng_hi = n_grid(P0 + t_last, W, D);
   const int ng_me = q_live ? n_grid(tqa, W, D) : 0;
@@ -682,33 +687,51 @@ __global__ __launch_bounds__(64 * (DH / 64)) void attn_f32_kernel(const AttnArgs
   const float* ak = W > 0 ? static_cast<const float*>(a.all_k) + (int64_t)b * a.arows * rowC + h * DH : nullptr;
   const float* av = W > 0 ? static_cast<const float*>(a.all_v) + (int64_t)b * a.arows * rowC + h * DH : nullptr;
 
-  float m_run = -INFINITY, l_run = 0.f;
-  for (int it = 0; it < ntile_g + ntile_w; ++it) {
-    const float* kb;
-    const float* vb;
-    int64_t stride;
-    int row0, nvalid;
-    const bool is_grid = it < ntile_g;
-    if (is_grid) {
-      kb = gk; vb = gv; stride = DH; row0 = it * kF32Keys; nvalid = ng_hi - row0;
+  // one float4 of K and one of V per lane and tile (row r, dims c..c+3); the
+  // next tile's are loaded while the current one is computed
+  static_assert(NT * 4 == kF32Keys * DH, "one float4 per lane and tile");
+  const int r = tid * 4 / DH;
+  const int c = tid * 4 - r * DH;
+  const int ntile = ntile_g + ntile_w;
+  // first key row of tile `it`: grid row, or all-state buffer row (absolute
+  // position - base) for a window tile; nvalid = rows of the tile in use
+  auto tile_rows = [&](int it, int& row0, int& nvalid) {
+    if (it < ntile_g) {
+      row0 = it * kF32Keys; nvalid = ng_hi - row0;
     } else {
-      // buffer row of the tile (absolute position - base)
-      kb = ak; vb = av; stride = rowC; row0 = j_lo + (it - ntile_g) * kF32Keys - a.base;
+      row0 = j_lo + (it - ntile_g) * kF32Keys - a.base;
       nvalid = P0 + t_last + 1 - (row0 + a.base);
     }
-    __syncthreads();
-    for (int e = tid * 4; e < kF32Keys * DH; e += NT * 4) {
-      const int r = e / DH;
-      const int c = e - r * DH;
-      float4 kw = make_float4(0.f, 0.f, 0.f, 0.f), vw = kw;
-      if (r < nvalid) {
-        kw = *reinterpret_cast<const float4*>(kb + (int64_t)(row0 + r) * stride + c);
-        vw = *reinterpret_cast<const float4*>(vb + (int64_t)(row0 + r) * stride + c);
-      }
-      *reinterpret_cast<float4*>(&sK[r][c]) = kw;
-      *reinterpret_cast<float4*>(&sV[r][c]) = vw;
+  };
+  auto fetch = [&](int it, float4& kw, float4& vw) {
+    int row0, nvalid;
+    tile_rows(it, row0, nvalid);
+    kw = make_float4(0.f, 0.f, 0.f, 0.f);
+    vw = kw;
+    if (r < nvalid) {
+      const bool g = it < ntile_g;
+      const int64_t off = (int64_t)(row0 + r) * (g ? (int64_t)DH : rowC) + c;
+      kw = *reinterpret_cast<const float4*>((g ? gk : ak) + off);
+      vw = *reinterpret_cast<const float4*>((g ? gv : av) + off);
     }
+  };
+  float4 kw, vw;
+  if (ntile > 0) fetch(0, kw, vw);
+
+  float m_run = -INFINITY, l_run = 0.f;
+  for (int it = 0; it < ntile; ++it) {
+    const bool is_grid = it < ntile_g;
+    int row0, nvalid;
+    tile_rows(it, row0, nvalid);
     __syncthreads();
+    *reinterpret_cast<float4*>(&sK[r][c]) = kw;
+    *reinterpret_cast<float4*>(&sV[r][c]) = vw;
+    __syncthreads();
+    if (it + 1 < ntile) fetch(it + 1, kw, vw);
+    // the tile's scores first (masked keys -inf), then one rescale of the
+    // running sums per tile and one exponential per key
+    float tmax = -INFINITY;
+#pragma unroll 4
     for (int kk = 0; kk < kF32Keys; ++kk) {
       bool valid;
       if (is_grid) {
@@ -719,25 +742,34 @@ __global__ __launch_bounds__(64 * (DH / 64)) void attn_f32_kernel(const AttnArgs
       }
       float sp = 0.f;
 #pragma unroll
-      for (int i = 0; i < 64; ++i) sp = fmaf(q[i], sK[kk][64 * part + i], sp);
-      if (TPQ == 2) sp += __shfl_xor(sp, 1);
-      if (valid) {   // uniform across the lanes of one query
-        const float sc = sp * a.sl2;
-        const float m_new = fmaxf(m_run, sc);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        const float p = __builtin_amdgcn_exp2f(sc - m_new);
-        l_run = l_run * alpha + p;
+      for (int i = 0; i < kF32Dims; ++i) sp = fmaf(q[i], sK[kk][d0 + i], sp);
 #pragma unroll
-        for (int i = 0; i < 64; ++i) acc[i] = fmaf(p, sV[kk][64 * part + i], acc[i] * alpha);
-        m_run = m_new;
+      for (int o = 1; o < TPQ; o <<= 1) sp += __shfl_xor(sp, o);
+      const float sc = valid ? sp * a.sl2 : -INFINITY;   // uniform across the lanes of one query
+      sS[kk][qi] = sc;   // every lane of a query stores the same value
+      tmax = fmaxf(tmax, sc);
+    }
+    if (tmax > -INFINITY) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m_run is -inf
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < kF32Dims; ++i) acc[i] *= alpha;
+#pragma unroll 4
+      for (int kk = 0; kk < kF32Keys; ++kk) {
+        const float p = __builtin_amdgcn_exp2f(sS[kk][qi] - m_new);   // 0 for a masked key
+        l_run += p;
+#pragma unroll
+        for (int i = 0; i < kF32Dims; ++i) acc[i] = fmaf(p, sV[kk][d0 + i], acc[i]);
       }
+      m_run = m_new;
     }
   }
   if (q_live) {
     const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-    float* op = static_cast<float*>(a.out) + ((int64_t)b * T + tq) * rowC + h * DH + 64 * part;
+    float* op = static_cast<float*>(a.out) + ((int64_t)b * T + tq) * rowC + h * DH + d0;
 #pragma unroll
-    for (int i = 0; i < 64; i += 4)
+    for (int i = 0; i < kF32Dims; i += 4)
       *reinterpret_cast<float4*>(op + i) = make_float4(acc[i] * inv, acc[i + 1] * inv, acc[i + 2] * inv, acc[i + 3] * inv);
   }
 }
@@ -808,9 +840,9 @@ hipError_t launch_prefill_attention(const AttnPlan& p, hipStream_t s) {
     a.n_qtiles = (p.T + 63) / 64;
     const int blocks = set_classes(p, a);
     if (p.Dh == 128)
-      hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(blocks), dim3(128), 0, s, a);
+      hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(blocks), dim3(64 * (128 / kF32Dims)), 0, s, a);
     else
-      hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(blocks), dim3(64), 0, s, a);
+      hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(blocks), dim3(64 * (64 / kF32Dims)), 0, s, a);
   }
   return hipGetLastError();
 }
