@@ -133,6 +133,13 @@ __device__ __forceinline__ bool better(float v, int j, float bv, int bi) {
 constexpr int kTileQ = 64;
 constexpr int kTileChunk = 32;
 
+// unsigned key with the order of the float scores (no NaN here); -0 and +0,
+// equal as scores, share one key
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f + 0.f);   // -0 + 0 = +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 template <int DH>
 __global__ __launch_bounds__(kAW * 64) void topk_select_tile_kernel(const TopkPlan p, int ncap) {
   extern __shared__ float s_tsc[];   // [kTileQ][ncap] candidate scores
@@ -221,15 +228,45 @@ __global__ __launch_bounds__(kAW * 64) void topk_select_tile_kernel(const TopkPl
     if (ncand <= p.topk) {
       for (int j = lane; j < ncand; j += 64) cp[j] = j + 1;
       base = ncand;
+    } else if (ncand <= 64) {
+      // one candidate per lane: the nsel-th highest score is found bit by bit
+      // on an order-preserving integer key (wave-wide ballot counts); kept
+      // are the candidates above it, then the lowest indices equal to it
+      const uint32_t key = lane < ncand ? order_key(row[lane]) : 0u;   // 0: below every real key
+      uint32_t thr = 0;
+#pragma unroll
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = thr | (1u << bit);
+        if (__builtin_popcountll(__ballot(key >= cand)) >= nsel) thr = cand;
+      }
+      const uint64_t gt = __ballot(key > thr);
+      uint64_t eq = __ballot(key == thr), take = 0;
+      for (int ties = nsel - __builtin_popcountll(gt); ties > 0; --ties) {
+        const uint64_t low = eq & (~eq + 1ull);
+        take |= low;
+        eq ^= low;
+      }
+      const uint64_t m = gt | take;   // nsel bits
+      if ((m >> lane) & 1ull) cp[__builtin_popcountll(m & ((1ull << lane) - 1ull))] = lane + 1;
+      base = nsel;
     } else {
       for (int j0 = 0; j0 < ncand; j0 += 64) {
         const int j = j0 + lane;
         const bool in = j < ncand;
         const float v = in ? row[j] : 0.f;
         int r = 0;
-        for (int i = 0; i < ncand; ++i) {
-          const float u = row[i];
-          r += (u > v || (u == v && i < j)) ? 1 : 0;
+        // the other candidates 64 at a time: one LDS read per lane, then each
+        // entry broadcast from its lane by a scalar read (no LDS round trip
+        // per comparison)
+        for (int i0 = 0; i0 < ncand; i0 += 64) {
+          const int ucnt = min(64, ncand - i0);
+          const int uc = __float_as_int(lane < ucnt ? row[i0 + lane] : 0.f);
+#pragma unroll 8
+          for (int ii = 0; ii < ucnt; ++ii) {
+            const float u = __int_as_float(__builtin_amdgcn_readlane(uc, ii));
+            const int i = i0 + ii;
+            r += (u > v || (u == v && i < j)) ? 1 : 0;
+          }
         }
         const bool kept = in && r < nsel;
         const uint64_t m = __ballot(kept);

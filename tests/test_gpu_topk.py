@@ -296,3 +296,29 @@ def test_topk_random(seed):
     (including the block-64 MFMA path when the draw allows it)."""
     B, H, Dh, block, topk, score, chunks, steps, dtype = _random_case(seed)
     _run(B, H, Dh, block, topk, score, chunks, steps, dtype, seed=6000 + seed)
+
+
+@pytest.mark.parametrize("score", [0, 1], ids=["quest", "moba"])
+def test_topk_prefill_tied_scores(score):
+    """A zero query (+0 in head 0, -0 in head 1) scores every candidate block
+    exactly 0 (as +0 or -0): ties go to the lower index, so each query keeps
+    blocks 1 .. min(k, candidates), in order.  T spans fewer and more than 64
+    candidates per query."""
+    R = need_gpu()
+    B, H, Dh, block, topk, T = 1, 2, 128, 64, 16, 64 * 72
+    max_pos = T + block
+    x = inputs.prefill_inputs(B, T, H, Dh, dtype=torch.bfloat16, mu=2.0, seed=41)
+    d = {n: t.contiguous().to(DEV) for n, t in x.items()}
+    d["q"] = torch.zeros_like(d["q"])
+    d["q"][:, :, 1] = -0.0
+    cache = R.topk_cache(B, H, Dh, max_pos, block, torch.bfloat16, DEV)
+    chosen = torch.full((B, T, H, topk), -7, dtype=torch.int32, device=DEV)
+    R.rat_topk_prefill(d["q"], d["k"], d["v"], d["zk"], d["zv"], cache, 0, max_pos, block, topk, score, chosen=chosen)
+    torch.cuda.synchronize()
+    got = chosen.cpu().numpy()
+    assert np.signbit(d["q"][0, 0, 1, 0].cpu().float().numpy())
+    for t in range(T):
+        nsel = min(topk, max(t // block - 1, 0))
+        want = list(range(1, nsel + 1)) + [-1] * (topk - nsel)
+        for h in range(H):
+            assert got[0, t, h].tolist() == want, (t, h, got[0, t, h].tolist())
