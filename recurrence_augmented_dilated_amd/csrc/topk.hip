@@ -43,28 +43,59 @@ __device__ __forceinline__ int64_t summary_off(int B, int64_t nbcap, int h, int 
   return (((int64_t)h * B + b) * nbcap + j) * 3 * Dh;
 }
 
-// ---- summaries of complete blocks: one workgroup of Dh threads per (h, b, j)
+// ---- summaries of complete blocks: one workgroup of 256 threads per
+// (h, b, j); a thread takes two adjacent dims of every G-th row of the block
+// (G = 512 / Dh row groups), the groups are combined in LDS in group order
+constexpr int kStatsThreads = 256;
+
 template <typename ET>
-__global__ void topk_stats_kernel(const TopkPlan p, int64_t j_lo, int64_t nj) {
+__global__ __launch_bounds__(kStatsThreads) void topk_stats_kernel(const TopkPlan p, int64_t j_lo, int64_t nj) {
+  __shared__ float s_red[3][2 * kStatsThreads];   // [min, max, sum][group * Dh + dim]
   const int64_t id = blockIdx.x;
   const int64_t jj = id % nj;
   const int64_t hb = id / nj;
   const int b = int(hb % p.B);
   const int h = int(hb / p.B);
   const int64_t j = j_lo + jj;
-  const int d = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int half = p.Dh / 2;
+  const int G = 2 * kStatsThreads / p.Dh;
+  const int rg = tid / half;
+  const int d = 2 * (tid - rg * half);
   const ET* src = static_cast<const ET*>(p.cache_k) + cache_off(p.B, p.max_pos, h, b, j * p.block, p.Dh) + d;
-  float mn = INFINITY, mx = -INFINITY, sum = 0.f;
-  for (int r = 0; r < p.block; ++r) {
-    const float x = ld1<ET>(src + (int64_t)r * p.Dh);
-    mn = fminf(mn, x);
-    mx = fmaxf(mx, x);
-    sum += x;
+  float mn0 = INFINITY, mx0 = -INFINITY, sm0 = 0.f, mn1 = INFINITY, mx1 = -INFINITY, sm1 = 0.f;
+#pragma unroll 4
+  for (int r = rg; r < p.block; r += G) {
+    float x0, x1;
+    if constexpr (sizeof(ET) == 2) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(src + (int64_t)r * p.Dh);
+      x0 = bf16_lo(w);
+      x1 = bf16_hi(w);
+    } else {
+      const float2 w = *reinterpret_cast<const float2*>(src + (int64_t)r * p.Dh);
+      x0 = w.x;
+      x1 = w.y;
+    }
+    mn0 = fminf(mn0, x0); mx0 = fmaxf(mx0, x0); sm0 += x0;
+    mn1 = fminf(mn1, x1); mx1 = fmaxf(mx1, x1); sm1 += x1;
   }
-  float* dst = p.summary + summary_off(p.B, p.max_pos / p.block, h, b, j, p.Dh) + d;
-  dst[0] = mn;
-  dst[p.Dh] = mx;
-  dst[2 * p.Dh] = sum / float(p.block);
+  const int o = rg * p.Dh + d;
+  s_red[0][o] = mn0; s_red[0][o + 1] = mn1;
+  s_red[1][o] = mx0; s_red[1][o + 1] = mx1;
+  s_red[2][o] = sm0; s_red[2][o + 1] = sm1;
+  __syncthreads();
+  if (tid < p.Dh) {
+    float mn = INFINITY, mx = -INFINITY, sum = 0.f;
+    for (int g = 0; g < G; ++g) {
+      mn = fminf(mn, s_red[0][g * p.Dh + tid]);
+      mx = fmaxf(mx, s_red[1][g * p.Dh + tid]);
+      sum += s_red[2][g * p.Dh + tid];
+    }
+    float* dst = p.summary + summary_off(p.B, p.max_pos / p.block, h, b, j, p.Dh) + tid;
+    dst[0] = mn;
+    dst[p.Dh] = mx;
+    dst[2 * p.Dh] = sum / float(p.block);
+  }
 }
 
 // ---- decode: state update, cache row, summary of a block the row completes
@@ -517,9 +548,9 @@ hipError_t launch_topk_stats(const TopkPlan& p, int64_t j_lo, int64_t j_hi, hipS
   if (nj <= 0) return hipSuccess;
   const int64_t blocks = (int64_t)p.H * p.B * nj;
   if (p.bf16)
-    hipLaunchKernelGGL(topk_stats_kernel<bf16_t>, dim3((unsigned)blocks), dim3(p.Dh), 0, s, p, j_lo, nj);
+    hipLaunchKernelGGL(topk_stats_kernel<bf16_t>, dim3((unsigned)blocks), dim3(kStatsThreads), 0, s, p, j_lo, nj);
   else
-    hipLaunchKernelGGL(topk_stats_kernel<float>, dim3((unsigned)blocks), dim3(p.Dh), 0, s, p, j_lo, nj);
+    hipLaunchKernelGGL(topk_stats_kernel<float>, dim3((unsigned)blocks), dim3(kStatsThreads), 0, s, p, j_lo, nj);
   return hipGetLastError();
 }
 
