@@ -1,17 +1,21 @@
 #!/usr/bin/env python3
 """Benchmark of the RAT+ dilated operator on one MI355X.
 
-Default run: the prefill workload B=1, 16 heads x 128, T=16384, D=16, W=128,
-bf16 (one step = one rat_dilated_prefill call: recurrence over keys and
-values plus dilated attention) gives `value` in tokens/s; the batched decode
-workload (batch 256, 16 x 128, context 32768, D=16, W=64, 1024 steps) is
-measured in the same run and reported under "decode".  Prints one JSON line.
+Default run (one JSON line): the long prefill B=1, 16 heads x 128,
+T=262144, D=64, W=0, bf16 (one step = one rat_dilated_prefill call:
+recurrence over keys and values plus dilated attention) gives `value` in
+tokens/s; the hybrid-head decode (batch 128, 32 heads x 128, context
+131072, D = 8 x 1, 12 x 16, 12 x 64, W=64, 1024 steps) is reported under
+"decode"; the tiny fp32 prefill, the T=16384 prefill and the batch-256
+decode under "other_configs".  Each workload carries the roofline of its
+kernels and a CPU baseline: the fp64 oracle over a pool of host cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps N]
-                    [--no-decode] [--no-cpu-baseline] [--config N]
+                    [--no-decode] [--no-other-configs] [--no-cpu-baseline]
+                    [--config N]
 
---config N measures one workload alone: 1-3 prefill (tiny fp32, the default,
-long), 4-5 decode (batched, hybrid heads), 6 chunked prefill, 7-8 top-k
+--config N measures one workload alone: 1-3 prefill (tiny fp32, T=16384,
+T=262144), 4-5 decode (batched, hybrid heads), 6 chunked prefill, 7-8 top-k
 decode and prefill, 9 RAT chunk-local prefill, 10 hybrid-head prefill.
 Inputs are seeded synthetic data generated on the GPU and resident in HBM
 before timing.
@@ -445,47 +449,136 @@ def aux_result(cfg_id, c, a, torch, R, inputs):
 
 
 # ---------------------------------------------------------------------------
-# CPU baseline: the fp64 oracle as it stands, one thread
+# CPU baseline: the fp64 oracle as it stands, over a pool of host cores
 # ---------------------------------------------------------------------------
 
-def cpu_baseline_prefill(c, x, torch, heads):
-    """The fp64 oracle on `heads` of the workload's heads (every query row, the
-    full-length recurrence), one thread; tokens/s scaled by H / len(heads).
-    With a per-head dilation list the sample is one head per dilation, each
-    time scaled by the number of heads with that dilation."""
-    import contextlib
-    import oracle
+def cpu_workers():
+    """Worker processes of the CPU baseline: the cores this process may run
+    on, at most 16 (one GPU's share of the host)."""
+    return max(1, min(len(os.sched_getaffinity(0)), 16))
+
+
+def cpu_model():
     try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
-    f = lambda t: t.float().cpu().double().numpy()  # noqa: E731
-    if isinstance(c["D"], list):
-        groups = [([h for h in range(c["H"]) if c["D"][h] == d][:1], c["D"].count(d), d)
-                  for d in sorted(set(c["D"]))]
-    else:
-        # at most ~2e8 (query, key) pairs of oracle work, at least one head
-        per_head = max(1, prefill_pairs(c["T"], c["D"], c["W"]) * c["B"])
-        heads = max(1, min(heads, c["H"], int(2e8 // per_head)))
-        groups = [(list(range(heads)), c["H"], c["D"])]
-    lim = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
-    sec = full = 0.0
-    with lim:
-        for hs, count, d in groups:
-            xs = {k: f(v[:, :, hs]) for k, v in x.items()}
-            t0 = time.perf_counter()
-            oracle.prefill(xs["q"], xs["k"], xs["v"], xs["zk"], xs["zv"], d, c["W"])
-            dt = time.perf_counter() - t0
-            log(f"[bench] cpu baseline: D={d}, {len(hs)} head(s): {dt:.1f} s")
-            sec += dt
-            full += dt * count / len(hs)
-    tok_s = c["B"] * c["T"] / full
-    n = sum(len(g[0]) for g in groups)
-    how = ("one head per dilation, each scaled by its head count" if isinstance(c["D"], list)
-           else f"tokens/s scaled by H/{n}")
-    return dict(value=tok_s, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"fp64 oracle prefill of {n} of {c['H']} heads (all {c['T']} query rows and the "
-                       f"full recurrence) took {sec:.1f} s on 1 thread; {how}")
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_prefill_head(task):
+    """Worker: one head of a prefill workload through the fp64 oracle, on
+    inputs drawn here with the workload's shapes and distributions.  Times
+    the full-length recurrence of keys and values and the attention of the
+    sampled query rows (one BLAS thread).  Returns (scan s, attention s,
+    sampled rows)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle
+    T, Dh, D, W, mu, seed, n_rows = task
+    with threadpool_limits(limits=1):
+        rng = np.random.default_rng(seed)
+        shp = (1, T, 1, Dh)
+        q, k, v = (rng.standard_normal(shp) for _ in range(3))
+        zk, zv = (mu + rng.standard_normal(shp) for _ in range(2))
+        t0 = time.perf_counter()
+        Kt = oracle.scan(k, zk)
+        Vt = oracle.scan(v, zv)
+        t1 = time.perf_counter()
+        rows = list(range(T)) if n_rows >= T else sorted(int(r) for r in rng.choice(T, n_rows, replace=False))
+        oracle.prefill(q, None, None, None, None, D, W, rows=rows, states=(Kt, Vt))
+        t2 = time.perf_counter()
+    return t1 - t0, t2 - t1, rows
+
+
+def _oracle_decode_seq(task):
+    """Worker: one sequence of a decode workload through the fp64 oracle's
+    DecodeCache (every head; caches filled from N(0, 1) here with the
+    workload's layout), `steps` steps from position ctx.  Returns the seconds
+    of the steps."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle
+    H, Dh, dil, W, ctx, max_pos, steps, mu, seed = task
+    with threadpool_limits(limits=1):
+        rng = np.random.default_rng(seed)
+        n = lambda *s: rng.standard_normal(s)  # noqa: E731
+        cache = oracle.DecodeCache(n(1, H, Dh), n(1, H, Dh), n(1, H, W, Dh), n(1, H, W, Dh),
+                                   [np.zeros((1, 1, Dh))] * H, [np.zeros((1, 1, Dh))] * H, dil, W)
+        # the grids are handed over as drawn (no second copy of ~2 GB)
+        cache.grid_k = [n(1, max_pos // d, Dh) for d in dil]
+        cache.grid_v = [n(1, max_pos // d, Dh) for d in dil]
+        xs = [(n(1, H, Dh), n(1, H, Dh), n(1, H, Dh), mu + n(1, H, Dh), mu + n(1, H, Dh)) for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i, (q, k, v, zk, zv) in enumerate(xs):
+            cache.step(q, k, v, zk, zv, [ctx + i])
+        return time.perf_counter() - t0
+
+
+def _pool_map(fn, tasks, n):
+    import multiprocessing as mp
+    with mp.get_context("spawn").Pool(n) as pool:
+        return pool.map(fn, tasks, chunksize=1)
+
+
+def cpu_baseline_prefill(c, n_rows):
+    """The fp64 oracle on every head of a prefill workload over a pool of
+    worker processes (one head per task): the full-length recurrence and
+    n_rows sampled query rows per head (every row if n_rows >= T), the
+    attention time extrapolated by the key-set pairs to every row.  tokens/s
+    = B T / (summed per-head seconds / workers)."""
+    import numpy as np
+    B, H, Dh, T, W = c["B"], c["H"], c["Dh"], c["T"], c["W"]
+    Ds = c["D"] if isinstance(c["D"], list) else [c["D"]] * H
+    tasks = [(T, Dh, Ds[h], W, c["mu"], 1000 + h, n_rows) for h in range(H)]
+    n = min(cpu_workers(), len(tasks))
+    t0 = time.perf_counter()
+    res = _pool_map(_oracle_prefill_head, tasks, n)
+    wall = time.perf_counter() - t0
+    total = 0.0
+    scan_s = attn_s = 0.0
+    for (ts, ta, rows), d in zip(res, Ds):
+        r = np.asarray(rows, dtype=np.int64)
+        sampled = int((np.maximum(0, r - W + 1) // d + np.minimum(W, r + 1)).sum())
+        full = prefill_pairs(T, d, W)
+        total += ts + ta * full / max(sampled, 1)
+        scan_s += ts
+        attn_s += ta
+    sec = B * total / n
+    measured = n_rows >= T
+    log(f"[bench] cpu baseline prefill: {H} heads over {n} workers, {wall:.1f} s wall "
+        f"(scan {scan_s:.1f} s, attention {attn_s:.1f} s summed)")
+    return dict(value=B * T / sec, unit="tokens/s", cores=n, kind="oracle", cpu_model=cpu_model(),
+                sample=(f"fp64 oracle, {n} worker processes x 1 BLAS thread, one head per task, all {H} heads: "
+                        f"the full {T}-step recurrence of keys and values and "
+                        + ("every query row (measured)" if measured else
+                           f"{n_rows} random query rows per head, the attention time scaled by key-set pairs "
+                           f"to all {T} rows (extrapolated)")
+                        + (f"; x B={B}" if B > 1 else "") + f"; inputs drawn on the host with the workload's "
+                        f"shapes and distributions; {wall:.1f} s wall"))
+
+
+def cpu_baseline_decode(c, n_seq, steps):
+    """The fp64 oracle's decode step for n_seq sequences (every head) over a
+    pool of worker processes, `steps` steps each from the workload's first
+    position.  tokens/s = sequence-steps / (summed step seconds / workers)."""
+    H, Dh, W, ctx = c["H"], c["Dh"], c["W"], c["ctx"]
+    max_pos = ctx + c["steps"]
+    tasks = [(H, Dh, c["D"], W, ctx, max_pos, steps, c["mu"], 2000 + i) for i in range(n_seq)]
+    n = min(cpu_workers(), len(tasks))
+    t0 = time.perf_counter()
+    secs = _pool_map(_oracle_decode_seq, tasks, n)
+    wall = time.perf_counter() - t0
+    rate = n_seq * steps / (sum(secs) / n)
+    log(f"[bench] cpu baseline decode: {n_seq} sequences x {steps} steps over {n} workers, {wall:.1f} s wall")
+    return dict(value=rate, unit="tokens/s", cores=n, kind="oracle", cpu_model=cpu_model(),
+                sample=(f"fp64 oracle DecodeCache.step, {n} worker processes x 1 BLAS thread: {n_seq} sequences "
+                        f"(all {H} heads, caches of context {ctx} drawn from N(0,1) on the host in the workload's "
+                        f"layout) x {steps} steps from position {ctx}; tokens/s = sequence-steps per summed "
+                        f"worker second x {n} workers (measured); {wall:.1f} s wall"))
 
 
 def measure_copy(torch):
@@ -600,7 +693,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=16, help="heads the CPU-baseline oracle run covers")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="default line only: skip the T=1024, T=16384 and batch-256 decode sub-results")
     ap.add_argument("--config", type=int, default=0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
@@ -639,81 +733,111 @@ def main():
     from recurrence_augmented_dilated_amd import inputs
     R.lib()
 
-    cfg_id = a.config or 2
-    c = CONFIGS[cfg_id]
-    if c["kind"] not in ("prefill", "decode"):
-        print(json.dumps(aux_result(cfg_id, c, a, torch, R, inputs)), flush=True)
+    if a.config:
+        c = CONFIGS[a.config]
+        if c["kind"] not in ("prefill", "decode"):
+            print(json.dumps(aux_result(a.config, c, a, torch, R, inputs)), flush=True)
+            return
+        fn = prefill_result if c["kind"] == "prefill" else decode_result
+        result = fn(a.config, c, a, torch, R, inputs, not a.no_cpu_baseline)
+        result["copy_GBps_measured"] = measure_copy(torch)
+        print(json.dumps(result), flush=True)
         return
-    result = {"metric": "prefill & decode tokens/s of RAT+ dilated op; % HBM/MFMA roofline",
-              "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True, "scaling": "weak",
-              "vs_baseline": None, "data": "synthetic"}
 
-    if c["kind"] == "prefill":
-        p = bench_prefill(c, a.steps, a.warmup, torch, R, inputs)
-        w = prefill_work(c)
-        tok_s = c["B"] * c["T"] / (p["ms"] * 1e-3)
-        scan_gbs = w["scan_bytes"] / (p["ms_scan"] * 1e-3)
-        attn_tfs = w["attn_flops"] / (p["ms_attn"] * 1e-3)
-        bf16 = c["dtype"] == "bf16"
-        attn_peak = PEAK_BF16 if bf16 else PEAK_F32_VALU
-        kernels = {
-            "scan": {"bound": "hbm", "ms": p["ms_scan"], "achieved": scan_gbs / 1e9, "peak": PEAK_HBM / 1e9,
-                     "unit": "GB/s", "frac": scan_gbs / PEAK_HBM, "algorithmic_bytes": w["scan_bytes"]},
-            "attention": {"bound": "mfma" if bf16 else "alu", "ms": p["ms_attn"], "achieved": attn_tfs / 1e12,
-                          "peak": attn_peak / 1e12, "unit": "TFLOP/s", "frac": attn_tfs / attn_peak,
-                          "algorithmic_flops": w["attn_flops"]},
-        }
-        dom = "scan" if p["ms_scan"] >= p["ms_attn"] else "attention"
-        k = kernels[dom]
-        # a per-head dilation list is named by its (dilation x heads) groups
-        dname = (c["D"] if not isinstance(c["D"], list) else
-                 ",".join(f"{d}x{c['D'].count(d)}" for d in sorted(set(c["D"]))))
-        wkey = f"prefill_T{c['T']}_D{str(dname).replace(',', '-')}_W{c['W']}"
-        result.update({
-            "value": tok_s, "steps": a.steps, "warmup": a.warmup, "ms_per_step": p["ms"],
-            "single_call_ms_per_step": p["ms_call"],
-            "single_call_ms_per_step_after": p["ms_call_after"],
-            "dtype": c["dtype"],
-            "config": {"workload": f"prefill B={c['B']} H={c['H']} Dh={c['Dh']} T={c['T']} D={dname} "
-                                   f"W={c['W']} {c['dtype']}", "config_id": cfg_id, "B": c["B"], "T": c["T"],
-                       "heads": c["H"], "head_dim": c["Dh"], "dilation": c["D"], "window": c["W"]},
-            "roofline": {"kernel": dom, "bound": k["bound"], "achieved": k["achieved"], "peak": k["peak"],
-                         "unit": k["unit"], "frac": k["frac"], "traffic": measured_traffic(dom, wkey)},
-            "kernels": kernels,
-            "ws_error": p["ws_error"],
-            "inputs_sha256": p["inputs_sha256"],
-            "copy_GBps_measured": measure_copy(torch),
-        })
-        for name in kernels:
-            kernels[name]["traffic"] = measured_traffic(name, wkey)
-        if not a.no_decode and a.config == 0:
-            cd = CONFIGS[4]
-            d = bench_decode(cd, a.decode_steps, 8, torch, R, inputs)
-            gbs = d["bytes_per_step"] / (d["ms"] * 1e-3)
-            result["decode"] = {
-                "workload": "decode B=256 H=16 Dh=128 ctx=32768 D=16 W=64 bf16", "steps": d["steps"],
-                "tokens_per_s": cd["B"] / (d["ms"] * 1e-3), "ms_per_step": d["ms"],
-                "roofline": {"kernel": "decode", "bound": "hbm", "achieved": gbs / 1e9, "peak": PEAK_HBM / 1e9,
-                             "unit": "GB/s", "frac": gbs / PEAK_HBM,
-                             "traffic": measured_traffic("decode", "decode_config4")},
-                "ws_error": d["ws_error"]}
-        if not a.no_cpu_baseline:
-            log("[bench] cpu baseline (oracle) ...")
-            result["cpu_baseline"] = cpu_baseline_prefill(c, p["x"], torch, min(a.cpu_heads, c["H"]))
-    else:
-        d = bench_decode(c, a.decode_steps, 8, torch, R, inputs)
-        gbs = d["bytes_per_step"] / (d["ms"] * 1e-3)
-        result.update({
-            "value": c["B"] / (d["ms"] * 1e-3), "steps": d["steps"], "warmup": 8, "ms_per_step": d["ms"],
-            "dtype": "bf16",
-            "config": {"workload": f"decode B={c['B']} H={c['H']} Dh={c['Dh']} ctx={c['ctx']} "
-                                   f"W={c['W']} dilation={sorted(set(c['D']))}", "config_id": cfg_id},
-            "roofline": {"kernel": "decode", "bound": "hbm", "achieved": gbs / 1e9, "peak": PEAK_HBM / 1e9,
-                         "unit": "GB/s", "frac": gbs / PEAK_HBM,
-                         "traffic": measured_traffic("decode", f"decode_config{cfg_id}")},
-            "ws_error": d["ws_error"],
-        })
+    # Default line: the longest prefill (T = 262144, the pages' prefill
+    # length) gives `value`; the hybrid-head decode (batch 128, context
+    # 131072) is reported under "decode"; the other three workloads under
+    # "other_configs".  Every workload carries its own roofline and CPU
+    # baseline.
+    cpu = not a.no_cpu_baseline
+    result = prefill_result(3, CONFIGS[3], a, torch, R, inputs, cpu)
+    result["copy_GBps_measured"] = measure_copy(torch)
+    if not a.no_decode:
+        result["decode"] = decode_result(5, CONFIGS[5], a, torch, R, inputs, cpu)
+    if not a.no_other_configs:
+        others = {}
+        for cid in (1, 2, 4):
+            c = CONFIGS[cid]
+            fn = prefill_result if c["kind"] == "prefill" else decode_result
+            others[str(cid)] = fn(cid, c, a, torch, R, inputs, cpu)
+        result["other_configs"] = others
     print(json.dumps(result), flush=True)
+
+
+METRIC = "prefill & decode tokens/s of RAT+ dilated op; % HBM/MFMA roofline"
+CPU_PREFILL_ROWS = {1: 1 << 30, 2: 1 << 30, 3: 2048, 10: 2048}   # query rows per head (>= T: all)
+CPU_DECODE_SAMPLE = {4: (16, 8), 5: (16, 2)}                      # (sequences, steps)
+
+
+def _free(torch):
+    import gc
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def prefill_result(cfg_id, c, a, torch, R, inputs, cpu):
+    """One prefill workload: tokens/s of the whole call, each kernel's
+    roofline, the dominant kernel's as `roofline`, and the CPU baseline."""
+    p = bench_prefill(c, a.steps, a.warmup, torch, R, inputs)
+    w = prefill_work(c)
+    tok_s = c["B"] * c["T"] / (p["ms"] * 1e-3)
+    scan_gbs = w["scan_bytes"] / (p["ms_scan"] * 1e-3)
+    attn_tfs = w["attn_flops"] / (p["ms_attn"] * 1e-3)
+    bf16 = c["dtype"] == "bf16"
+    attn_peak = PEAK_BF16 if bf16 else PEAK_F32_VALU
+    # a per-head dilation list is named by its (dilation x heads) groups
+    dname = (c["D"] if not isinstance(c["D"], list) else
+             ",".join(f"{d}x{c['D'].count(d)}" for d in sorted(set(c["D"]))))
+    wkey = f"prefill_T{c['T']}_D{str(dname).replace(',', '-')}_W{c['W']}"
+    kernels = {
+        "scan": {"bound": "hbm", "ms": p["ms_scan"], "achieved": scan_gbs / 1e9, "peak": PEAK_HBM / 1e9,
+                 "unit": "GB/s", "frac": scan_gbs / PEAK_HBM, "algorithmic_bytes": w["scan_bytes"],
+                 "traffic": measured_traffic("scan", wkey)},
+        "attention": {"bound": "mfma" if bf16 else "alu", "ms": p["ms_attn"], "achieved": attn_tfs / 1e12,
+                      "peak": attn_peak / 1e12, "unit": "TFLOP/s", "frac": attn_tfs / attn_peak,
+                      "algorithmic_flops": w["attn_flops"], "traffic": measured_traffic("attention", wkey)},
+    }
+    dom = "scan" if p["ms_scan"] >= p["ms_attn"] else "attention"
+    k = kernels[dom]
+    res = {"metric": METRIC, "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "data": "synthetic",
+           "value": tok_s, "steps": a.steps, "warmup": a.warmup, "ms_per_step": p["ms"],
+           "single_call_ms_per_step": p["ms_call"], "single_call_ms_per_step_after": p["ms_call_after"],
+           "dtype": c["dtype"],
+           "config": {"workload": f"prefill B={c['B']} H={c['H']} Dh={c['Dh']} T={c['T']} D={dname} "
+                                  f"W={c['W']} {c['dtype']}", "config_id": cfg_id, "B": c["B"], "T": c["T"],
+                      "heads": c["H"], "head_dim": c["Dh"], "dilation": c["D"], "window": c["W"]},
+           "roofline": {"kernel": dom, "bound": k["bound"], "achieved": k["achieved"], "peak": k["peak"],
+                        "unit": k["unit"], "frac": k["frac"], "traffic": k["traffic"]},
+           "kernels": kernels, "ws_error": p["ws_error"], "inputs_sha256": p["inputs_sha256"]}
+    del p
+    _free(torch)
+    if cpu:
+        res["cpu_baseline"] = cpu_baseline_prefill(c, CPU_PREFILL_ROWS.get(cfg_id, 2048))
+    return res
+
+
+def decode_result(cfg_id, c, a, torch, R, inputs, cpu):
+    """One decode workload: tokens/s over the timed steps, the HBM roofline
+    of the step and the CPU baseline."""
+    d = bench_decode(c, a.decode_steps, 8, torch, R, inputs)
+    _free(torch)
+    gbs = d["bytes_per_step"] / (d["ms"] * 1e-3)
+    dname = ",".join(f"{x}x{c['D'].count(x)}" for x in sorted(set(c["D"])))
+    res = {"metric": METRIC, "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "data": "synthetic",
+           "value": c["B"] / (d["ms"] * 1e-3), "steps": d["steps"], "warmup": 8, "ms_per_step": d["ms"],
+           "dtype": "bf16",
+           "config": {"workload": f"decode B={c['B']} H={c['H']} Dh={c['Dh']} ctx={c['ctx']} W={c['W']} "
+                                  f"dilation={dname} bf16, {d['steps']} steps", "config_id": cfg_id},
+           "roofline": {"kernel": "decode", "bound": "hbm", "achieved": gbs / 1e9, "peak": PEAK_HBM / 1e9,
+                        "unit": "GB/s", "frac": gbs / PEAK_HBM, "algorithmic_bytes_per_step": d["bytes_per_step"],
+                        "traffic": measured_traffic("decode", f"decode_config{cfg_id}")},
+           "ws_error": d["ws_error"]}
+    if cpu:
+        n_seq, steps = CPU_DECODE_SAMPLE.get(cfg_id, (8, 4))
+        res["cpu_baseline"] = cpu_baseline_decode(c, n_seq, steps)
+    return res
 
 
 if __name__ == "__main__":

@@ -28,7 +28,16 @@
  *     Its first 256 bytes are a header; the 32-bit word at byte offset 8 is a
  *     sticky error word: bit 1 = a decode position was outside [0, max_pos)
  *     (that sequence's output is zero and its cache is untouched).  Zero the
- *     word to reset it.
+ *     word to reset it.  The 32-bit word at byte offset 12 is the recurrence
+ *     scan's look-back poll limit, written by the caller (never by the
+ *     library): 0, as zero-filled, selects the default; n > 0 makes a scan
+ *     block wait at most n - 1 polls for an earlier chunk's published carry
+ *     before it computes that chunk's aggregate itself from the inputs (the
+ *     results agree up to fp32 rounding; n = 1 takes that path on every
+ *     wait, which the tests use to exercise it).  Every entry point that
+ *     runs a scan reads it: rat_scan, rat_dilated_prefill(_stage),
+ *     rat_prefill_chunk, rat_local_prefill_chunk, rat_topk_prefill.  Nothing
+ *     else in the library depends on state outside the call's arguments.
  *   - All work is asynchronous on `stream`.  The returned status covers
  *     argument validation (done on the host before any HIP call) and launch
  *     errors; device faults surface at the caller's next synchronization.
@@ -84,7 +93,10 @@ const char* rat_last_error(void);
  *           position j with (j + 1) mod E == 0 (E = 1: all states; E = D:
  *           the dilated grid)
  *   h_last  [B][H][Dh]     fp32 or NULL  state at position T - 1
- *   ws      workspace of at least rat_scan_workspace_size(B, T, H, Dh) bytes
+ *   ws      workspace of at least rat_scan_workspace_size(B, T, H, Dh) bytes:
+ *           the look-back words through which chunks of the sequence hand
+ *           their carries to later chunks (the one-pass scan needs them; the
+ *           caller owns them so that the library never allocates)
  * T = 0 is a no-op (buffers may then be NULL).  States and h_last come from
  * one fp32 carry chain.
  * ------------------------------------------------------------------------ */

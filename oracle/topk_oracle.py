@@ -22,8 +22,8 @@ What it computes (sources are the pages' titles plus the section named):
              take for a key inside the box [min, max];
     MoBA  -- the mean (mean-pooled keys); the score is q . mean.
 * Key set of the query at position t.  The first block and the query's own
-  (local) block l = t // block, the latter up to position t, are always kept
-  (the methods keep them "according to their original designs").  Among the
+  (local) block l = t // block, the latter up to position t, are always kept,
+  as each selection method does in its own design.  Among the
   complete blocks strictly between them, 1 .. l-1, the `topk` with the
   highest scores are added.  Readings taken where the pages are silent: the
   K selected blocks come in addition to the first and local blocks; ties go
@@ -137,9 +137,3 @@ def topk_prefill(q, k, v, zk, zv, block: int, topk: int, method: str, scale=None
                 out[b, t, h] = attend_selected(q[b, t, h], Kt[b, :, h], Vt[b, :, h], t, block, sel, scale)
     return out, chosen
 
-
-def candidate_scores(q_row, kmin, kmax, kmean, t: int, block: int, method: str) -> np.ndarray:
-    """Scores of the candidate blocks 1 .. t//block - 1 of one query (index
-    0 of the result is block 1); stats [nb, Dh] of one (b, h)."""
-    local = t // block
-    return np.array([block_score(q_row, kmin[j], kmax[j], kmean[j], method) for j in range(1, local)])

@@ -19,7 +19,7 @@ __all__ = [
     "RatError", "lib", "rat_scan", "rat_scan_workspace_size", "rat_dilated_prefill",
     "rat_dilated_prefill_stage",
     "rat_dilated_prefill_workspace_size", "rat_grid_layout", "rat_decode_step",
-    "rat_decode_workspace_size", "workspace", "workspace_error", "LIB_PATH",
+    "rat_decode_workspace_size", "workspace", "workspace_error", "workspace_set_poll_limit", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librat.so")
@@ -167,6 +167,14 @@ def workspace(nbytes: int, device, key="default") -> torch.Tensor:
 def workspace_error(ws: torch.Tensor) -> int:
     """The sticky device error word of a workspace (synchronises)."""
     return int(ws[8:12].view(torch.int32).item())
+
+
+def workspace_set_poll_limit(ws: torch.Tensor, polls=None) -> None:
+    """Set the workspace header's look-back poll limit (byte offset 12):
+    None restores the library default; polls = n makes a scan block wait for
+    at most n polls of an unpublished predecessor before it computes that
+    predecessor's chunk itself (0: on every wait)."""
+    ws[12:16].view(torch.int32).fill_(0 if polls is None else int(polls) + 1)
 
 
 def _per_head(dilation, H):

@@ -18,8 +18,8 @@
 // each wave streams its share of rows, LPK = Dh/8 lanes per key (one 16-byte
 // bf16 load per lane per row), with a private online softmax per key slot
 // and DPP reductions for the dot products; waves merge in LDS.  Items with
-// several splits write (m, l, acc) partials that a second kernel merges in a
-// fixed order.  Heads are launched heaviest first (per-head dilation).
+// several splits write (m, l, acc) partials, one slot per work item, that a
+// second kernel merges in a fixed order.  Heads are launched heaviest first (per-head dilation).
 #include "rat_internal.h"
 #include "kv_stream.h"
 
@@ -40,7 +40,7 @@ struct DecArgs {
   void* out;
   float* partials;
   uint32_t* hdr;
-  int B, H, W, max_split;
+  int B, H, W;
   float sl2;
   int reset_every;
   DecodeHeads heads;
@@ -234,7 +234,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(const DecArgs a) {
       for (int i = 0; i < 8; ++i) o8[i] = fin.acc[i] * inv;
       R::store(static_cast<ET*>(a.out) + bh * DH + 8 * c, o8);
     } else {
-      float* pp = a.partials + (bh * a.max_split + s) * (DH + 2);
+      // partials of work item `item`: the splits of one (b, h) are adjacent
+      float* pp = a.partials + (int64_t)item * (DH + 2);
 #pragma unroll
       for (int i = 0; i < 8; ++i) pp[8 * c + i] = fin.acc[i];
       if (c == 0) { pp[DH] = fin.m; pp[DH + 1] = fin.l; }
@@ -246,10 +247,15 @@ template <typename ET, int DH>
 __global__ __launch_bounds__(DH) void decode_combine(const DecArgs a) {
   const int bhi = blockIdx.x;
   const int h = bhi % a.H;
+  const int b = bhi / a.H;
   const int ns = a.heads.nsplit[h];
   if (ns <= 1) return;
   const int d = threadIdx.x;
-  const float* pp = a.partials + (int64_t)bhi * a.max_split * (DH + 2);
+  // the first work item of (b, h): head h's launch rank, then b's splits
+  int oi = 0;
+  while (oi + 1 < a.H && a.heads.order[oi] != h) ++oi;
+  const int64_t item0 = (int64_t)a.heads.item_base[oi] + (int64_t)b * ns;
+  const float* pp = a.partials + item0 * (DH + 2);
   float M = -INFINITY;
   for (int s = 0; s < ns; ++s) M = fmaxf(M, pp[s * (DH + 2) + DH]);
   float L = 0.f, O = 0.f;
@@ -284,7 +290,7 @@ hipError_t launch_decode(const DecodePlan& p, hipStream_t s) {
   a.ring_k = p.ring_k; a.ring_v = p.ring_v;
   a.pos = p.pos; a.max_pos = p.max_pos; a.out = p.out;
   a.partials = p.partials; a.hdr = p.hdr;
-  a.B = p.B; a.H = p.H; a.W = p.W; a.max_split = p.max_split;
+  a.B = p.B; a.H = p.H; a.W = p.W;
   a.sl2 = p.scale * 1.4426950408889634f;
   a.reset_every = p.reset_every;
   a.heads = p.heads;

@@ -109,14 +109,6 @@ PrefillCarve prefill_carve(int32_t B, int32_t T, int32_t H, int32_t Dh, const in
   return c;
 }
 
-// Look-back polls before a block recomputes an unpublished predecessor
-// itself.  RAT_SCAN_FALLBACK_SPINS overrides the default (tests force 0 to
-// exercise the recompute path).
-int scan_fallback_spins() {
-  const char* e = std::getenv("RAT_SCAN_FALLBACK_SPINS");
-  return e ? std::atoi(e) : -1;
-}
-
 // Decode split plan: a (b, h) item streams at most ~4096 grid rows per split,
 // and small batches are split further so that the launch has >= 2048 items.
 constexpr int kMaxSplit = 256;
@@ -234,7 +226,6 @@ rat_status_t rat_scan(const void* x, const float* z, const float* h0, void* stat
   p.bf16 = dt == RAT_BF16;
   p.heads.dil[0] = store_every;
   p.ws = ws;
-  p.fallback_spins = scan_fallback_spins();
   hipError_t e = rat::launch_scan(p, stream);
   if (e != hipSuccess) return fail(RAT_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
   return ok();
@@ -298,7 +289,6 @@ rat_status_t rat_dilated_prefill_stage(rat_prefill_stage_t stage, const void* q,
   sp.arows = T;
   sp.bf16 = bf16;
   sp.ws = ws;
-  sp.fallback_spins = scan_fallback_spins();
   if (stage != RAT_STAGE_ATTENTION) {
     hipError_t e = rat::launch_scan(sp, stream);
     if (e != hipSuccess) return fail(RAT_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
@@ -431,7 +421,6 @@ static rat_status_t prefill_chunk_impl(const void* q, const void* k, const void*
   sp.bf16 = bf16;
   sp.heads = cache;
   sp.ws = ws;
-  sp.fallback_spins = scan_fallback_spins();
   e = rat::launch_scan(sp, stream);
   if (e != hipSuccess) return fail(RAT_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
   // the chunk's last min(W, T) states into the ring: a launch of its own for
@@ -535,7 +524,10 @@ size_t rat_decode_workspace_size(int32_t B, int32_t H, int32_t Dh, const int32_t
   int32_t nsplit[RAT_MAX_HEADS];
   int32_t max_split;
   decode_splits(B, H, dilation, W, max_pos, nsplit, max_split);
-  return sizeof(rat::WsHeader) + align_up((size_t)B * H * max_split * (Dh + 2) * sizeof(float));
+  // one (m, l, acc[Dh]) partial per work item (b, h, split)
+  size_t items = 0;
+  for (int h = 0; h < H; ++h) items += (size_t)B * nsplit[h];
+  return sizeof(rat::WsHeader) + align_up(items * (Dh + 2) * sizeof(float));
 }
 
 static rat_status_t decode_step_impl(const void* q, const void* k, const void* v, const float* zk,
@@ -544,7 +536,7 @@ static rat_status_t decode_step_impl(const void* q, const void* k, const void* v
                              void* ring_k, void* ring_v, const int32_t* pos, int64_t max_pos,
                              void* out, int32_t B, int32_t H, int32_t Dh, const int32_t* dilation,
                              int32_t W, float scale, rat_dtype_t dt, void* ws, size_t ws_bytes,
-                             hipStream_t stream, int32_t reset_every) {
+                             hipStream_t stream, int32_t reset_every, bool check_only) {
   rat_status_t st = check_common(B, 0, H, Dh, dt);
   if (st != RAT_OK) return st;
   if (W < 0) return fail(RAT_ERR_INVALID_ARG, "W must be >= 0 (got %d)", W);
@@ -569,6 +561,7 @@ static rat_status_t decode_step_impl(const void* q, const void* k, const void* v
   if ((st = check_ptr(ring_v, "ring_v", W == 0)) != RAT_OK) return st;
   const size_t need = rat_decode_workspace_size(B, H, Dh, dilation, W, max_pos);
   if (ws_bytes < need) return fail(RAT_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (check_only) return ok();
 
   rat::DecodePlan p;
   std::memset(&p, 0, sizeof(p));
@@ -618,8 +611,9 @@ rat_status_t rat_decode_step(const void* q, const void* k, const void* v, const 
                              void* ring_k, void* ring_v, const int32_t* pos, int64_t max_pos,
                              void* out, int32_t B, int32_t H, int32_t Dh, const int32_t* dilation,
                              int32_t W, float scale, rat_dtype_t dt, void* ws, size_t ws_bytes,
-                             hipStream_t stream) {  return decode_step_impl(q, k, v, zk, zv, state_k, state_v, grid_k, grid_v, grid_off, grid_cap, ring_k, ring_v,
-                          pos, max_pos, out, B, H, Dh, dilation, W, scale, dt, ws, ws_bytes, stream, 0);
+                             hipStream_t stream) {
+  return decode_step_impl(q, k, v, zk, zv, state_k, state_v, grid_k, grid_v, grid_off, grid_cap, ring_k, ring_v,
+                          pos, max_pos, out, B, H, Dh, dilation, W, scale, dt, ws, ws_bytes, stream, 0, false);
 }
 
 }  // extern "C"
@@ -728,7 +722,6 @@ rat_status_t rat_topk_prefill(const void* q, const void* k, const void* v, const
   sp.bf16 = bf16;
   dense_cache_table(H, max_pos, sp.heads);
   sp.ws = ws;
-  sp.fallback_spins = scan_fallback_spins();
   e = rat::launch_scan(sp, stream);
   if (e != hipSuccess) return fail(RAT_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
 
@@ -890,7 +883,7 @@ rat_status_t rat_local_decode_step(const void* q, const void* k, const void* v, 
   if (!local_dilation(H, L, dil))
     return fail(RAT_ERR_INVALID_ARG, "need 1 <= H <= %d and L >= 1 (got H = %d, L = %d)", RAT_MAX_HEADS, H, L);
   return decode_step_impl(q, k, v, zk, zv, state_k, state_v, grid_k, grid_v, grid_off, grid_cap, ring_k, ring_v,
-                          pos, max_pos, out, B, H, Dh, dil, 1, scale, dt, ws, ws_bytes, stream, L);
+                          pos, max_pos, out, B, H, Dh, dil, 1, scale, dt, ws, ws_bytes, stream, L, false);
 }
 
 }  // extern "C"

@@ -75,9 +75,10 @@ __device__ __forceinline__ int64_t grid_row_offset(const HeadTable& ht, int B, i
 // Workspace header (first 256 bytes of every workspace).
 struct WsHeader {
   uint32_t reserved;
-  uint32_t epoch;    // scan: call counter; tags published carries
-  uint32_t error;    // sticky bit set: a device-side check failed (see rat.h)
-  uint32_t pad[61];
+  uint32_t epoch;       // scan: call counter; tags published carries
+  uint32_t error;       // sticky bit set: a device-side check failed (see rat.h)
+  uint32_t poll_limit;  // caller-set: 0 = default look-back polls, n > 0 = n - 1 polls
+  uint32_t pad[60];
 };
 static_assert(sizeof(WsHeader) == 256, "header size");
 
@@ -140,7 +141,6 @@ struct ScanPlan {
   int bf16;            // 1: x and outputs are bf16; 0: fp32
   HeadTable heads;
   void* ws;            // workspace base (header + look-back arrays)
-  int fallback_spins;  // look-back polls before a local recompute (< 0: default)
 };
 
 size_t scan_workspace_bytes(int ntensors, int B, int T, int H, int Dh);

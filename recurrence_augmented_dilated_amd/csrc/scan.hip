@@ -43,6 +43,7 @@ constexpr int kChunkT = kLW * kNW;   // time steps per block
 constexpr int kWin = 2;              // predecessors read per look-back round trip
 constexpr int kSparseMaxD = 32;      // largest D whose column grid is staged through LDS
 constexpr uint32_t kFallbackSpins = 256;   // default polls before computing a predecessor locally
+                                           // (the workspace header's poll_limit word overrides it)
 
 // Hide a register value from the optimiser (an empty asm that "modifies"
 // it), so that pass 2 recomputes the gates instead of keeping pass 1's.
@@ -123,7 +124,6 @@ struct ScanArgs {
   uint64_t* agg_b;
   uint64_t* incl;
   uint32_t* hdr;
-  uint32_t fallback_spins;
   HeadTable heads;
 };
 
@@ -183,6 +183,10 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t ticket = blockIdx.x;
   const uint32_t epoch = a.hdr[1];
+  // polls of an unpublished predecessor before its aggregate is computed
+  // locally: the workspace header's poll_limit (n > 0: n - 1), else the default
+  const uint32_t poll_word = a.hdr[3];
+  const uint32_t fallback_spins = poll_word ? poll_word - 1u : kFallbackSpins;
 
   const int chunk = int(ticket / uint32_t(a.n_slabs));
   const int slab = int(ticket - uint32_t(chunk) * uint32_t(a.n_slabs));
@@ -312,7 +316,7 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
         j -= used;
         if (used > 0) {
           spins = 0;
-        } else if (++spins > a.fallback_spins) {
+        } else if (++spins > fallback_spins) {
           // predecessor j shows no progress: fold its chunk in directly
           const int chg = cs * SC + cl;
           float Aj, Bj;
@@ -581,7 +585,6 @@ hipError_t launch_scan(const ScanPlan& p, hipStream_t s) {
   a.arows = p.arows > 0 ? p.arows : p.T;
   a.reset_every = p.reset_every;
   a.heads = p.heads;
-  a.fallback_spins = p.fallback_spins >= 0 ? uint32_t(p.fallback_spins) : kFallbackSpins;
   const int nc = pick_nc(a.C);
   a.slabs_per_bt = a.C / (64 * nc);
   a.n_slabs = p.ntensors * p.B * a.slabs_per_bt;

@@ -223,14 +223,13 @@ def test_topk_prefill_lists_in_workspace():
     assert torch.equal(outs[0], outs[1])
 
 
-def test_topk_prefill_full_size_sampled():
-    """T = 4096, 16 x 128, block 64, top-16 MoBA (the top-k prefill workload):
-    sampled rows against the oracle's attention over the kernel's (validated)
-    choice."""
+def _sampled_prefill(B, H, Dh, T, block, topk, score, seed, rows, what, mu=2.0):
+    """One rat_topk_prefill call from position 0 over T rows; the chosen
+    lists and outputs of the sampled (b, t, h) rows are checked against the
+    oracle (validated choice, attention over it)."""
     R = need_gpu()
-    B, H, Dh, T, block, topk, score = 1, 16, 128, 4096, 64, 16, 1
     max_pos = T + block
-    x = inputs.prefill_inputs(B, T, H, Dh, dtype=torch.bfloat16, mu=2.0, seed=38)
+    x = inputs.prefill_inputs(B, T, H, Dh, dtype=torch.bfloat16, mu=mu, seed=seed)
     q = f64(x["q"])
     Kt = oracle.scan(f64(x["k"]), f64(x["zk"]))
     Vt = oracle.scan(f64(x["v"]), f64(x["zv"]))
@@ -243,11 +242,45 @@ def test_topk_prefill_full_size_sampled():
     torch.cuda.synchronize()
     o = f64(out)
     c = chosen.cpu().numpy()
+    _verify([o[b, t, h] for b, t, h in rows], [c[b, t, h] for b, t, h in rows], q, Kt, Vt, rows, block, topk,
+            METHODS[score], BF16_TOL, TK.block_stats(Kr, block), what)
+
+
+def test_topk_prefill_full_size_sampled():
+    """T = 4096, 16 x 128, block 64, top-16 MoBA (the top-k prefill workload):
+    sampled rows against the oracle's attention over the kernel's (validated)
+    choice."""
+    T, H = 4096, 16
     rng = np.random.default_rng(39)
     rows = [(0, int(t), int(h)) for t, h in zip(rng.integers(0, T, 256), rng.integers(0, H, 256))]
     rows += [(0, T - 1, 0), (0, 0, 1), (0, 63, 2), (0, 64, 3)]
-    _verify([o[b, t, h] for b, t, h in rows], [c[b, t, h] for b, t, h in rows], q, Kt, Vt, rows, block, topk,
-            TK.MOBA, BF16_TOL, TK.block_stats(Kr, block), "prefill T=4096 sampled")
+    _sampled_prefill(1, H, 128, T, 64, 16, 1, 38, rows, "prefill T=4096 sampled")
+
+
+def _long_rows(T, H, seed):
+    """The last rows (the most candidates), rows at block edges and random rows."""
+    rng = np.random.default_rng(seed)
+    ts = {T - 1, T - 2, T - 63, T - 64, T - 65, 0, 63, 64, 127, 128, 4095, 4096}
+    ts.update(int(t) for t in rng.integers(T // 2, T, 96))
+    ts.update(int(t) for t in rng.integers(0, T, 32))
+    return [(0, t, h) for t in sorted(ts) for h in range(H)]
+
+
+@pytest.mark.parametrize("score", [0, 1], ids=["quest", "moba"])
+def test_topk_prefill_tile_select_at_its_limit(score):
+    """T = 64 * 257, the longest sequence the per-tile selection kernel takes
+    (its candidate summaries fill the most LDS: 255 candidates per query)."""
+    T, H = 64 * 257, 2
+    _sampled_prefill(1, H, 128, T, 64, 16, score, 51 + score, _long_rows(T, H, 52), f"prefill T={T} tile select")
+
+
+@pytest.mark.parametrize("score", [0, 1], ids=["quest", "moba"])
+def test_topk_prefill_per_query_select_branch(score):
+    """T = 64 * 258, one block past the per-tile selection's limit: the lists
+    come from the per-query selection pass (written, attention skipped), then
+    the MFMA attention walks them."""
+    T, H = 64 * 258, 2
+    _sampled_prefill(1, H, 128, T, 64, 16, score, 53 + score, _long_rows(T, H, 54), f"prefill T={T} per-query select")
 
 
 def test_topk_prefill_many_candidates_sampled():
