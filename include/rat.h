@@ -249,6 +249,38 @@ rat_status_t rat_decode_step(const void* q, const void* k, const void* v, const 
                              void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
+ * rat_decode_step_noalloc -- rat_decode_step without a workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * operation, arguments and kernels as rat_decode_step; its scratch (the
+ * split-K partials) is a fixed array of RAT_DECODE_SCRATCH_BYTES that the
+ * library holds in each GPU's memory from load until the process ends.  The
+ * call allocates nothing.
+ *   - A step whose rat_decode_workspace_size(...) exceeds
+ *     RAT_DECODE_SCRATCH_BYTES returns RAT_ERR_WORKSPACE before anything
+ *     runs (the hybrid-head batch-128 decode at context 131072 needs about
+ *     21 MB).
+ *   - `stream` must belong to the current device (else
+ *     RAT_ERR_INVALID_ARG); the first call on a device looks up that
+ *     device's scratch address.
+ *   - Every call on a GPU shares that GPU's scratch: calls that overlap on
+ *     one GPU (concurrent streams, threads) race and must be serialised by
+ *     the caller.  Nothing in the scratch needs to start at zero.
+ *   - A position outside [0, max_pos) still yields a zero output and leaves
+ *     that sequence's cache untouched; its sticky error bit lands in the
+ *     scratch, which the caller cannot read (use rat_decode_step with a
+ *     workspace to observe it).
+ * ------------------------------------------------------------------------ */
+#define RAT_DECODE_SCRATCH_BYTES (32u << 20)
+rat_status_t rat_decode_step_noalloc(const void* q, const void* k, const void* v, const float* zk,
+                                     const float* zv, float* state_k, float* state_v, void* grid_k,
+                                     void* grid_v, const int64_t* grid_off, const int32_t* grid_cap,
+                                     void* ring_k, void* ring_v, const int32_t* pos, int64_t max_pos,
+                                     void* out, int32_t B, int32_t H, int32_t Dh,
+                                     const int32_t* dilation, int32_t W, float scale, rat_dtype_t dtype,
+                                     hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
  * RAT's chunk-local variant ("RAT: Bridging RNN Efficiency and Attention
  * Accuracy via Chunk-based Sequence Modeling", approach): the recurrence runs
  * inside chunks of L positions, restarting from a zero state at every

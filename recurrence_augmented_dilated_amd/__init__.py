@@ -19,7 +19,8 @@ __all__ = [
     "RatError", "lib", "rat_scan", "rat_scan_workspace_size", "rat_dilated_prefill",
     "rat_dilated_prefill_stage",
     "rat_dilated_prefill_workspace_size", "rat_grid_layout", "rat_decode_step",
-    "rat_decode_workspace_size", "workspace", "workspace_error", "workspace_set_poll_limit", "LIB_PATH",
+    "rat_decode_workspace_size", "rat_decode_step_noalloc", "DECODE_SCRATCH_BYTES", "workspace",
+    "workspace_error", "workspace_set_poll_limit", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librat.so")
@@ -77,6 +78,9 @@ def lib():
             L.rat_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                           c_i64, vp, c_int, c_int, c_int, vp, c_int, c_f, c_int,
                                           vp, c_sz, vp]
+            L.rat_decode_step_noalloc.restype = c_int
+            L.rat_decode_step_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                  c_i64, vp, c_int, c_int, c_int, vp, c_int, c_f, c_int, vp]
             L.rat_prefill_chunk_workspace_size.restype = c_sz
             L.rat_prefill_chunk_workspace_size.argtypes = [c_int, c_int, c_int, c_int, vp, c_int, c_i64, c_int]
             L.rat_prefill_chunk.restype = c_int
@@ -288,6 +292,31 @@ def rat_decode_step(q, k, v, zk, zv, state_k, state_v, grid_k, grid_v, grid_off,
         _ptr(q), _ptr(k), _ptr(v), _ptr(zk), _ptr(zv), _ptr(state_k), _ptr(state_v), _ptr(grid_k),
         _ptr(grid_v), off, cap, _ptr(ring_k), _ptr(ring_v), _ptr(pos), int(max_pos), _ptr(out), B, H,
         Dh, _i32_array(dil), int(W), s, _dtype_code(q), _ptr(ws), ws.numel(), _stream(q.device)))
+    return out
+
+
+DECODE_SCRATCH_BYTES = 32 << 20   # RAT_DECODE_SCRATCH_BYTES in include/rat.h
+
+
+def rat_decode_step_noalloc(q, k, v, zk, zv, state_k, state_v, grid_k, grid_v, grid_off, grid_cap,
+                            ring_k, ring_v, pos, max_pos, dilation, W, scale=None, out=None):
+    """rat_decode_step without a workspace: the library's built-in scratch
+    (DECODE_SCRATCH_BYTES per GPU) holds the split partials.  Calls that
+    overlap on one GPU race; `out` must be given by callers that cannot
+    allocate (else it is allocated here)."""
+    B, H, Dh = q.shape
+    dil = _per_head(dilation, H)
+    if pos.dtype != torch.int32:
+        raise TypeError("pos must be int32")
+    if out is None:
+        out = torch.empty_like(q)
+    off = (ctypes.c_int64 * H)(*[int(x) for x in grid_off])
+    cap = _i32_array(grid_cap)
+    s = -1.0 if scale is None else float(scale)
+    _check(lib().rat_decode_step_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(zk), _ptr(zv), _ptr(state_k), _ptr(state_v), _ptr(grid_k),
+        _ptr(grid_v), off, cap, _ptr(ring_k), _ptr(ring_v), _ptr(pos), int(max_pos), _ptr(out), B, H,
+        Dh, _i32_array(dil), int(W), s, _dtype_code(q), _stream(q.device)))
     return out
 
 

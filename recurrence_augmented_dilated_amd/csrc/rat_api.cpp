@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "rat_internal.h"
 
@@ -33,6 +34,46 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---------------------------------------------------------------------------
+// Scratch of rat_decode_step_noalloc (its workspace header and split-K
+// partials): one fixed array in every GPU's memory, loaded with the library,
+// so that the call allocates nothing.  Host code never passes `scratch` to a
+// kernel (its name is a host-side stand-in there): the device address comes
+// from hipGetSymbolAddress, once per device, with that device current.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoallocScratchBytes = RAT_DECODE_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of this device's scratch; the stream must belong to
+// the current device.
+rat_status_t noalloc_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(RAT_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(RAT_ERR_UNSUPPORTED, "device %d (at most %d devices)", dev, kMaxDevices);
+  if (stream) {
+    hipDevice_t sd = -1;
+    e = hipStreamGetDevice(stream, &sd);
+    if (e != hipSuccess) return fail(RAT_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+    if ((int)sd != dev)
+      return fail(RAT_ERR_INVALID_ARG, "the stream belongs to device %d, the current device is %d", (int)sd, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(RAT_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return RAT_OK;
+}
 
 size_t elt_size(rat_dtype_t dt) { return dt == RAT_BF16 ? 2 : 4; }
 
@@ -614,6 +655,36 @@ rat_status_t rat_decode_step(const void* q, const void* k, const void* v, const 
                              hipStream_t stream) {
   return decode_step_impl(q, k, v, zk, zv, state_k, state_v, grid_k, grid_v, grid_off, grid_cap, ring_k, ring_v,
                           pos, max_pos, out, B, H, Dh, dilation, W, scale, dt, ws, ws_bytes, stream, 0, false);
+}
+
+rat_status_t rat_decode_step_noalloc(const void* q, const void* k, const void* v, const float* zk,
+                                     const float* zv, float* state_k, float* state_v, void* grid_k,
+                                     void* grid_v, const int64_t* grid_off, const int32_t* grid_cap,
+                                     void* ring_k, void* ring_v, const int32_t* pos, int64_t max_pos,
+                                     void* out, int32_t B, int32_t H, int32_t Dh,
+                                     const int32_t* dilation, int32_t W, float scale, rat_dtype_t dt,
+                                     hipStream_t stream) {
+  // every argument is validated on the host first, with the scratch standing
+  // in for the workspace (a placeholder address: nothing is launched here)
+  rat_status_t st = check_common(B, 0, H, Dh, dt);
+  if (st != RAT_OK) return st;
+  if (W >= 0 && max_pos >= 1 && check_dilation(dilation, H) == RAT_OK) {
+    const size_t need = rat_decode_workspace_size(B, H, Dh, dilation, W, max_pos);
+    if (need > kNoallocScratchBytes)
+      return fail(RAT_ERR_WORKSPACE,
+                  "this step needs %zu bytes of scratch; rat_decode_step_noalloc has %zu "
+                  "(use rat_decode_step with a workspace)", need, kNoallocScratchBytes);
+  }
+  void* const placeholder = reinterpret_cast<void*>(uintptr_t(kAlign));
+  st = decode_step_impl(q, k, v, zk, zv, state_k, state_v, grid_k, grid_v, grid_off, grid_cap, ring_k, ring_v,
+                        pos, max_pos, out, B, H, Dh, dilation, W, scale, dt, placeholder, kNoallocScratchBytes,
+                        stream, 0, true);
+  if (st != RAT_OK) return st;
+  void* ws = nullptr;
+  if ((st = noalloc_scratch(stream, &ws)) != RAT_OK) return st;
+  return decode_step_impl(q, k, v, zk, zv, state_k, state_v, grid_k, grid_v, grid_off, grid_cap, ring_k, ring_v,
+                          pos, max_pos, out, B, H, Dh, dilation, W, scale, dt, ws, kNoallocScratchBytes, stream, 0,
+                          false);
 }
 
 }  // extern "C"
