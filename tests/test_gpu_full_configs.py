@@ -95,7 +95,7 @@ def _planted_inputs(T, H, Dh, Ds, W, n_plant, seed):
     other keys and every other channel stay N(0, 1).  A planted key then
     scores ~34 nats above the unplanted ones at the default scale and 5.7
     nats above the previous planted key, so each row's output is essentially
-    the value of the latest planted key in its key set.  Planted positions
+    the value (N(0, 1/4)) of the latest planted key in its key set.  Planted positions
     are spread over the sequence at least W + 2 apart and sit, per a random
     draw, on the grid of every head (p = D_max - 1 mod D_max), on the grid of
     the denser heads only, next to the grid (p = 0 or D - 2 mod D: never a
@@ -120,7 +120,7 @@ def _planted_inputs(T, H, Dh, Ds, W, n_plant, seed):
     g = torch.Generator(device=DEV).manual_seed(seed)
     q = torch.randn((1, T, H, Dh), generator=g, device=DEV)
     k = torch.randn((1, T, H, Dh), generator=g, device=DEV)
-    v = torch.randn((1, T, H, Dh), generator=g, device=DEV)
+    v = 0.5 * torch.randn((1, T, H, Dh), generator=g, device=DEV)   # outputs ~v: bf16 half-ulps below 1e-2
     q[..., 0] = 16.0
     pidx = torch.tensor(plant, device=DEV)
     k[0, pidx, :, 0] = (4.0 * (12 + torch.arange(len(plant), device=DEV, dtype=torch.float32)))[:, None]
