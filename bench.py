@@ -675,11 +675,21 @@ def summarize_trace(trace_dir, kernel, workload, bench_args):
              f"{bench_args}",
              f"$ python3 bench.py --summarize-trace {trace_dir} {kernel} {workload} --pmc-bench-args '{bench_args}'",
              ""]
+    # per-dispatch durations from the trace: the median, and the mean without
+    # the first three (cold) dispatches, next to the --stats figures
+    import statistics
+    with open(_find_csv(trace_dir, "kernel_trace.csv")) as fh:
+        trace = [r for r in csv.DictReader(fh) if pat in r["Kernel_Name"]]
     for r in rows:
+        ds = [(int(t["End_Timestamp"]) - int(t["Start_Timestamp"])) / 1e3 for t in trace
+              if t["Kernel_Name"] == r["Name"]]
         lines += [f"kernel: {r['Name']}",
                   f"calls {int(float(r['Calls']))}, average {float(r['AverageNs']) / 1e3:.2f} us, "
                   f"min {float(r['MinNs']) / 1e3:.2f} us, max {float(r['MaxNs']) / 1e3:.2f} us, "
                   f"{float(r['Percentage']):.2f}% of the run's kernel time"]
+        if len(ds) > 3:
+            lines += [f"per-dispatch trace: median {statistics.median(ds):.2f} us, "
+                      f"mean after the first 3 dispatches {statistics.mean(ds[3:]):.2f} us"]
     with open(os.path.join(ROOT, "profiles", f"{kernel}_{workload}_kernel_trace.txt"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
