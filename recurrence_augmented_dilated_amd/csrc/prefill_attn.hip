@@ -518,16 +518,6 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
   using Slot1 = std::integral_constant<int, 1>;
   using Slot2 = std::integral_constant<int, 2>;
   using Slot3 = std::integral_constant<int, 3>;
-  auto tile = [&](int it, auto S) __attribute__((always_inline)) {
-    constexpr int slot = decltype(S)::value;
-    bool is_grid, needed, masked;
-    int kbase;
-    tile_info(it, is_grid, needed, masked, kbase);
-    if (needed) {
-      scores(sK[slot], sc);
-      finish(it, sV[slot], sc);
-    }
-  };
 
   wait_vmcnt<0>();   // Q fragments are in registers before the ring starts
   if (W > 0) {
@@ -545,10 +535,19 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
       constexpr int sa = decltype(SA)::value;
       constexpr int sb = decltype(SB)::value;
       // the next pair goes into the slots of the previous one
-      if (t0 + 2 < ntiles) issue(t0 + 2, sK[sa ^ 2], sV[sa ^ 2]);
-      if (t0 + 3 < ntiles) issue(t0 + 3, sK[sb ^ 2], sV[sb ^ 2]);
-      tile(t0, SA);
-      if (t0 + 1 < ntiles) tile(t0 + 1, SB);
+      // each tile of the next pair goes out once a tile of this pair has
+      // its products under way
+      auto tile_then = [&](int it, auto S, int nxt, char* dK, char* dV) __attribute__((always_inline)) {
+        constexpr int slot = decltype(S)::value;
+        bool is_grid, needed, masked;
+        int kbase;
+        tile_info(it, is_grid, needed, masked, kbase);
+        if (needed) scores(sK[slot], sc);
+        if (nxt < ntiles) issue(nxt, dK, dV);
+        if (needed) finish(it, sV[slot], sc);
+      };
+      tile_then(t0, SA, t0 + 2, sK[sa ^ 2], sV[sa ^ 2]);
+      if (t0 + 1 < ntiles) tile_then(t0 + 1, SB, t0 + 3, sK[sb ^ 2], sV[sb ^ 2]);
       wait_vmcnt<0>();
       ring_barrier();
     };
@@ -579,9 +578,18 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
     auto step = [&](int it, auto S) __attribute__((always_inline)) {
       constexpr int slot = decltype(S)::value;
       // tile it + kAhead goes into the slot of tile it - 1
-      if (it + kAhead < ntiles) issue(it + kAhead, sK[(slot + kAhead) & 3], sV[(slot + kAhead) & 3]);
       if constexpr (SEL) sel_advance(it);
-      tile(it, S);
+      {
+        bool is_grid, needed, masked;
+        int kbase;
+        tile_info(it, is_grid, needed, masked, kbase);
+        if (needed) scores(sK[slot], sc);
+        // the loads of tile it + kAhead go out once this tile's products are
+        // under way (issued right after the barrier, the block's 32 loads
+        // queue ahead of every wave's first MFMA)
+        if (it + kAhead < ntiles) issue(it + kAhead, sK[(slot + kAhead) & 3], sV[(slot + kAhead) & 3]);
+        if (needed) finish(it, sV[slot], sc);
+      }
       // tile it+1 must have landed; later tiles may still fly
       const int later = min(ntiles - 1, it + kAhead) - (it + 1);
       if (later >= 2) wait_vmcnt<2 * LPW>();

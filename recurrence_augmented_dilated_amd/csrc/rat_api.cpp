@@ -131,8 +131,18 @@ void prefill_grid_layout(int32_t T, int32_t H, const int32_t* dilation, bool bf1
 
 int64_t prefill_tpad(int32_t T) { return ((int64_t)T + 63) / 64 * 64; }
 
+// A prefill without a window whose every head has D >= kSegMinD stores grid
+// states only: its scan runs segmented, with an (A, B) pair per grid element
+// in the workspace.
+bool prefill_segmented(int32_t H, const int32_t* dilation, int32_t W) {
+  if (W != 0) return false;
+  for (int h = 0; h < H; ++h)
+    if (dilation[h] < rat::kSegMinD) return false;
+  return true;
+}
+
 struct PrefillCarve {
-  size_t scan_bytes, grid_bytes, allk_bytes, allv_bytes, total;
+  size_t scan_bytes, grid_bytes, allk_bytes, allv_bytes, part_bytes, total;
 };
 
 PrefillCarve prefill_carve(int32_t B, int32_t T, int32_t H, int32_t Dh, const int32_t* dilation,
@@ -146,7 +156,8 @@ PrefillCarve prefill_carve(int32_t B, int32_t T, int32_t H, int32_t Dh, const in
   c.grid_bytes = align_up((size_t)B * rows * Dh * elt_size(dt));
   c.allk_bytes = W > 0 ? align_up((size_t)B * T * H * Dh * elt_size(dt)) : 0;
   c.allv_bytes = W > 0 ? align_up((size_t)B * H * Dh * (bf16 ? prefill_tpad(T) : T) * elt_size(dt)) : 0;
-  c.total = c.scan_bytes + 2 * c.grid_bytes + c.allk_bytes + c.allv_bytes;
+  c.part_bytes = prefill_segmented(H, dilation, W) ? align_up((size_t)B * rows * Dh * 2 * sizeof(float)) : 0;
+  c.total = c.scan_bytes + 2 * c.grid_bytes + c.allk_bytes + c.allv_bytes + 2 * c.part_bytes;
   return c;
 }
 
@@ -315,12 +326,17 @@ rat_status_t rat_dilated_prefill_stage(rat_prefill_stage_t stage, const void* q,
   void* grid_v = base + cv.scan_bytes + cv.grid_bytes;
   void* all_k = W > 0 ? base + cv.scan_bytes + 2 * cv.grid_bytes : nullptr;
   void* all_v = W > 0 ? base + cv.scan_bytes + 2 * cv.grid_bytes + cv.allk_bytes : nullptr;
+  char* part = base + cv.scan_bytes + 2 * cv.grid_bytes + cv.allk_bytes + cv.allv_bytes;
   const bool bf16 = dt == RAT_BF16;
 
   rat::ScanPlan sp;
   std::memset(&sp, 0, sizeof(sp));
   int64_t rows;
   prefill_grid_layout(T, H, dilation, bf16, W, sp.heads, rows);
+  if (cv.part_bytes) {
+    sp.part[0] = reinterpret_cast<float*>(part);
+    sp.part[1] = reinterpret_cast<float*>(part + cv.part_bytes);
+  }
   sp.ten[0] = {k, zk, nullptr, all_k, grid_k, nullptr, rat::kAllToken, rat::kGridHeadRow};
   sp.ten[1] = {v, zv, nullptr, all_v, grid_v, nullptr, bf16 ? rat::kAllHeadCol : rat::kAllToken,
                bf16 ? rat::kGridHeadCol : rat::kGridHeadRow};

@@ -141,8 +141,21 @@ struct ScanPlan {
   int bf16;            // 1: x and outputs are bf16; 0: fp32
   HeadTable heads;
   void* ws;            // workspace base (header + look-back arrays)
+  // Optional (null: unused): per tensor, room for one (A, B) fp32 pair per
+  // grid element, in the row-major order of the grid (kGridHeadRow or
+  // kGridToken indexing; kGridHeadCol grids index it as kGridHeadRow).  With
+  // it, a scan that stores only grid states (no all-state output, no restart,
+  // every stored D >= 16) runs as a segmented scan.
+  float* part[2];
 };
 
+// Smallest dilation of a grid-only scan that runs segmented (at most one grid
+// position in each wave's steps).
+constexpr int kSegMinD = 16;
+
+// Whether a scan plan stores grid states only, with D >= kSegMinD wherever a
+// grid is stored: the segmented scan then applies, given part[].
+bool scan_grid_only(const ScanPlan& p);
 size_t scan_workspace_bytes(int ntensors, int B, int T, int H, int Dh);
 hipError_t launch_scan(const ScanPlan& p, hipStream_t s);
 

@@ -40,6 +40,7 @@ namespace {
 constexpr int kLW = 16;              // time steps per wave
 constexpr int kNW = 8;               // waves per block
 constexpr int kChunkT = kLW * kNW;   // time steps per block
+static_assert(kSegMinD >= kLW, "a grid-only wave holds at most one grid position");
 constexpr int kWin = 2;              // predecessors read per look-back round trip
 constexpr int kSparseMaxD = 32;      // largest D whose column grid is staged through LDS
 constexpr uint32_t kFallbackSpins = 256;   // default polls before computing a predecessor locally
@@ -124,6 +125,9 @@ struct ScanArgs {
   uint64_t* agg_b;
   uint64_t* incl;
   uint32_t* hdr;
+  float* part[2];     // segmented scan: (A, B) pairs per grid element and tensor
+  int n_seg;          // segmented scan: segments per slab
+  int seg_chunks;     // segmented scan: chunks per segment
   HeadTable heads;
 };
 
@@ -163,6 +167,90 @@ __device__ void chunk_aggregate(const XT* x, const float* z, int64_t C, int T, i
     Bv = g * Bv + c * xv;
     A *= g;
   }
+}
+
+// Carry into chunk `chunk` of a slab for channel cl of the slab (one thread
+// per channel): publishes the chunk's aggregate (A, Bv), then walks back over
+// the predecessors' published words until an inclusive state is found,
+// folding in the aggregates on the way (or computing a silent predecessor's
+// aggregate from its inputs after fallback_spins polls).  Chunk 0 starts
+// from h0.
+template <typename XT, bool RESET, int SC>
+__device__ __forceinline__ float chunk_carry(const ScanArgs& a, const ScanTensor& tn, uint32_t ticket, int chunk,
+                                             int slab, int b, int cs, int cl, float A, float Bv, uint32_t epoch,
+                                             uint32_t fallback_spins) {
+  const int64_t C = a.C;
+  const int T = a.T;
+  const int64_t widx = (int64_t)ticket * SC + cl;
+  float carry = 0.f;
+  if (chunk == 0) {
+    const int chg = cs * SC + cl;
+    const int hh = chg / a.Dh;
+    carry = tn.h0 ? tn.h0[((int64_t)b * a.H + hh) * a.Dh + (chg - hh * a.Dh)] : 0.f;
+  } else {
+    publish(a.agg_a + widx, tag_word(A, epoch));
+    publish(a.agg_b + widx, tag_word(Bv, epoch));
+    float accA = 1.f, accB = 0.f;
+    int j = chunk - 1;
+    uint32_t spins = 0;
+    bool done = false;
+    while (!done) {
+      uint64_t wi[kWin], wa[kWin], wb[kWin];
+#pragma unroll
+      for (int i = 0; i < kWin; ++i) {
+        const int jj = j - i;
+        if (jj >= 0) {
+          const int64_t pidx = ((int64_t)jj * a.n_slabs + slab) * SC + cl;
+          wi[i] = peek(a.incl + pidx);
+          wa[i] = peek(a.agg_a + pidx);
+          wb[i] = peek(a.agg_b + pidx);
+        } else {
+          wi[i] = wa[i] = wb[i] = 0;
+        }
+      }
+      int used = 0;
+      bool stop = false;
+#pragma unroll
+      for (int i = 0; i < kWin; ++i) {
+        if (!stop && !done) {
+          if (uint32_t(wi[i] >> 32) == epoch) {
+            carry = accA * word_value(wi[i]) + accB;
+            done = true;
+          } else if (uint32_t(wa[i] >> 32) == epoch && uint32_t(wb[i] >> 32) == epoch) {
+            accB = accA * word_value(wb[i]) + accB;
+            accA *= word_value(wa[i]);
+            ++used;
+          } else {
+            stop = true;
+          }
+        }
+      }
+      if (done) break;
+      j -= used;
+      if (used > 0) {
+        spins = 0;
+      } else if (++spins > fallback_spins) {
+        // predecessor j shows no progress: fold its chunk in directly
+        const int chg = cs * SC + cl;
+        float Aj, Bj;
+        chunk_aggregate<XT, RESET>(static_cast<const XT*>(tn.x) + (int64_t)b * T * C + chg,
+                                   tn.z + (int64_t)b * T * C + chg, C, T, j, a.p0, a.reset_every, Aj, Bj);
+        accB = accA * Bj + accB;
+        accA *= Aj;
+        if (j == 0) {
+          const int hh = chg / a.Dh;
+          const float h0v = tn.h0 ? tn.h0[((int64_t)b * a.H + hh) * a.Dh + (chg - hh * a.Dh)] : 0.f;
+          carry = accA * h0v + accB;
+          done = true;
+        }
+        --j;
+        spins = 0;
+      } else {
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+  }
+  return carry;
 }
 
 template <typename XT, int NC, bool RESET>
@@ -269,74 +357,7 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
       A *= Aw;
     }
     const int64_t widx = (int64_t)ticket * SC + cl;
-    float carry;
-    if (chunk == 0) {
-      const int chg = cs * SC + cl;
-      const int hh = chg / a.Dh;
-      carry = tn.h0 ? tn.h0[((int64_t)b * a.H + hh) * a.Dh + (chg - hh * a.Dh)] : 0.f;
-    } else {
-      publish(a.agg_a + widx, tag_word(A, epoch));
-      publish(a.agg_b + widx, tag_word(Bv, epoch));
-      float accA = 1.f, accB = 0.f;
-      int j = chunk - 1;
-      uint32_t spins = 0;
-      bool done = false;
-      while (!done) {
-        uint64_t wi[kWin], wa[kWin], wb[kWin];
-#pragma unroll
-        for (int i = 0; i < kWin; ++i) {
-          const int jj = j - i;
-          if (jj >= 0) {
-            const int64_t pidx = ((int64_t)jj * a.n_slabs + slab) * SC + cl;
-            wi[i] = peek(a.incl + pidx);
-            wa[i] = peek(a.agg_a + pidx);
-            wb[i] = peek(a.agg_b + pidx);
-          } else {
-            wi[i] = wa[i] = wb[i] = 0;
-          }
-        }
-        int used = 0;
-        bool stop = false;
-#pragma unroll
-        for (int i = 0; i < kWin; ++i) {
-          if (!stop && !done) {
-            if (uint32_t(wi[i] >> 32) == epoch) {
-              carry = accA * word_value(wi[i]) + accB;
-              done = true;
-            } else if (uint32_t(wa[i] >> 32) == epoch && uint32_t(wb[i] >> 32) == epoch) {
-              accB = accA * word_value(wb[i]) + accB;
-              accA *= word_value(wa[i]);
-              ++used;
-            } else {
-              stop = true;
-            }
-          }
-        }
-        if (done) break;
-        j -= used;
-        if (used > 0) {
-          spins = 0;
-        } else if (++spins > fallback_spins) {
-          // predecessor j shows no progress: fold its chunk in directly
-          const int chg = cs * SC + cl;
-          float Aj, Bj;
-          chunk_aggregate<XT, RESET>(static_cast<const XT*>(tn.x) + (int64_t)b * T * C + chg,
-                              tn.z + (int64_t)b * T * C + chg, C, T, j, a.p0, a.reset_every, Aj, Bj);
-          accB = accA * Bj + accB;
-          accA *= Aj;
-          if (j == 0) {
-            const int hh = chg / a.Dh;
-            const float h0v = tn.h0 ? tn.h0[((int64_t)b * a.H + hh) * a.Dh + (chg - hh * a.Dh)] : 0.f;
-            carry = accA * h0v + accB;
-            done = true;
-          }
-          --j;
-          spins = 0;
-        } else {
-          __builtin_amdgcn_s_sleep(2);
-        }
-      }
-    }
+    const float carry = chunk_carry<XT, RESET, SC>(a, tn, ticket, chunk, slab, b, cs, cl, A, Bv, epoch, fallback_spins);
     publish(a.incl + widx, tag_word(A * carry + Bv, epoch));
     float cw = carry;
 #pragma unroll
@@ -544,6 +565,306 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
   }
 }
 
+// Segmented scan for grid-only outputs (no all-state output, no restart,
+// every stored grid with D >= kLW, so a wave's kLW steps hold at most one
+// grid position).  Block = (segment, slab): a contiguous run of seg_chunks
+// chunks of one slab, walked in order with the next chunk's inputs in flight
+// while the current one is folded.  Phase A: per chunk, each wave folds its
+// steps into its aggregate and the partial aggregate up to its grid position;
+// one thread per channel keeps the segment's running aggregate and hands
+// every wave the aggregate from the segment start to the wave's first step,
+// so each grid position gets its (A, B) relative to the segment start,
+// written to part[] (state = A * carry_in + B).  The segment's aggregate then
+// goes through the same decoupled look-back as the chunked scan, over
+// segments instead of chunks (a handful per slab, all resident at once), and
+// phase B turns the pairs into grid states with one FMA each.  Every input
+// element is read once; part[] adds 8 bytes per grid element written and
+// read.
+template <typename XT, int NC>
+__global__ __launch_bounds__(kNW * 64) void scan_seg_kernel(const ScanArgs a) {
+  using V = XVec<XT, NC>;
+  using Z = XVec<float, NC>;
+  constexpr int SC = 64 * NC;   // channels per slab
+  static_assert(SC <= kNW * 64, "one prefix thread per channel");
+  __shared__ float s_A[kNW][SC];
+  __shared__ float s_B[kNW][SC];
+  __shared__ float s_PA[kNW][SC];   // aggregate from the segment start to each wave's first step
+  __shared__ float s_PB[kNW][SC];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t epoch = a.hdr[1];
+  const uint32_t poll_word = a.hdr[3];
+  // segments publish about together; a wait this long means a segment that
+  // is not running (the device is shared), whose aggregate is then computed
+  // here from its inputs
+  const uint32_t fallback_spins = poll_word ? poll_word - 1u : kFallbackSpins * 256u;
+  const int64_t C = a.C;
+  const int T = a.T;
+  const int n_chunks = int(((int64_t)T + kChunkT - 1) / kChunkT);
+  const int seg = int(blockIdx.x) / a.n_slabs;
+  const int slab = int(blockIdx.x) - seg * a.n_slabs;
+  const int per_tensor = a.B * a.slabs_per_bt;
+  const int ti = slab / per_tensor;
+  const int rem = slab - ti * per_tensor;
+  const int b = rem / a.slabs_per_bt;
+  const int cs = rem - b * a.slabs_per_bt;
+  const ScanTensor tn = ti == 0 ? a.ten[0] : a.ten[1];
+  float* const part = ti == 0 ? a.part[0] : a.part[1];
+  const int lo = lane * NC;
+  const int ch = cs * SC + lo;   // first channel of this lane in [0, C)
+  const int h = ch / a.Dh;
+  const int d = ch - h * a.Dh;
+  const int D = tn.grid_mode == kGridToken ? a.heads.dil[0] : a.heads.dil[h];
+  const int c_begin = seg * a.seg_chunks;
+  const int c_end = min(n_chunks, c_begin + a.seg_chunks);
+  XT* const out_grid = tn.grid_mode != kGridToken && a.heads.gcap[h] == 0 ? nullptr
+                                                                          : static_cast<XT*>(tn.out_grid);
+  const int64_t G_tok = T / D;
+  // element index of grid entry i of this lane's first channel (row-major)
+  auto grid_elem = [&](int64_t i) __attribute__((always_inline)) -> int64_t {
+    return tn.grid_mode == kGridToken ? (((int64_t)b * G_tok + i) * a.H + h) * a.Dh + d
+                                      : grid_row_offset(a.heads, a.B, b, h, i, a.Dh) + d;
+  };
+  // the grid position in the kLW steps from row t0, as (step offset or -1, entry)
+  auto grid_at = [&](int t0, int& gs, int64_t& gi) __attribute__((always_inline)) {
+    const int64_t ja0 = a.p0 + t0;
+    int64_t nxt = (ja0 / D) * D + (D - 1);
+    if (nxt < ja0) nxt += D;
+    const int64_t off = nxt - ja0;
+    gs = (out_grid && off < kLW && t0 + off < T) ? int(off) : -1;
+    gi = (nxt + 1) / D - 1;
+  };
+
+  const XT* xbase = static_cast<const XT*>(tn.x) + (int64_t)b * T * C + cs * SC;
+  const float* zbase = tn.z + (int64_t)b * T * C + cs * SC;
+  typename V::raw xr[kLW];
+  typename Z::raw zr[kLW];
+  // this wave's kLW steps of chunk c (c >= n_chunks: nothing is read)
+  auto load = [&](int c) __attribute__((always_inline)) {
+    const int t0 = c * kChunkT + wave * kLW;
+#pragma unroll
+    for (int s = 0; s < kLW; ++s) {
+      const int t = t0 + s;
+      if (t < T) {
+        xr[s] = V::load(xbase + (int64_t)t * C + lo);
+        zr[s] = Z::load(zbase + (int64_t)t * C + lo);
+      } else {
+        xr[s] = V::zero();
+        zr[s] = Z::zero();
+      }
+    }
+  };
+
+  // ---- phase A
+  float segA = 1.f, segB = 0.f;            // prefix thread: the segment's running aggregate
+  float lA[NC], lB[NC];                    // the lane holding T-1: its aggregate from the segment start
+#pragma unroll
+  for (int c = 0; c < NC; ++c) { lA[c] = 1.f; lB[c] = 0.f; }
+  load(c_begin);
+  for (int c = c_begin; c < c_end; ++c) {
+    const int t0 = c * kChunkT + wave * kLW;
+    int gs;
+    int64_t gi;
+    grid_at(t0, gs, gi);
+    const int ls = (tn.h_last && t0 <= T - 1 && T - 1 < t0 + kLW) ? T - 1 - t0 : -1;
+    float hl[NC], pp[NC], gA[NC], gB[NC], qA[NC], qB[NC];
+#pragma unroll
+    for (int k = 0; k < NC; ++k) { hl[k] = 0.f; pp[k] = 1.f; gA[k] = qA[k] = 1.f; gB[k] = qB[k] = 0.f; }
+#pragma unroll
+    for (int s = 0; s < kLW; ++s) {
+      const bool live = (t0 + s) < T;
+#pragma unroll
+      for (int k = 0; k < NC; ++k) {
+        float cc = gate_comp(Z::get(zr[s], k));
+        float g = 1.f - cc;
+        if (!live) { g = 1.f; cc = 0.f; }
+        hl[k] = g * hl[k] + cc * V::get(xr[s], k);
+        pp[k] *= g;
+        gA[k] = s == gs ? pp[k] : gA[k];
+        gB[k] = s == gs ? hl[k] : gB[k];
+        qA[k] = s == ls ? pp[k] : qA[k];
+        qB[k] = s == ls ? hl[k] : qB[k];
+        // taken here, step by step (else every step's products stay live
+        // for a selection at the end)
+        opaque(gA[k]); opaque(gB[k]); opaque(qA[k]); opaque(qB[k]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NC; ++k) { s_A[wave][lo + k] = pp[k]; s_B[wave][lo + k] = hl[k]; }
+    // the next chunk's inputs land while this one is folded (past the
+    // segment's last chunk: a chunk index past the sequence, nothing read)
+    load(c + 1 < c_end ? c + 1 : n_chunks);
+    __syncthreads();
+    if (tid < SC) {
+      float pA = segA, pB = segB;
+#pragma unroll
+      for (int w = 0; w < kNW; ++w) {
+        s_PA[w][tid] = pA;
+        s_PB[w][tid] = pB;
+        const float Aw = s_A[w][tid];
+        pB = Aw * pB + s_B[w][tid];
+        pA *= Aw;
+      }
+      segA = pA;
+      segB = pB;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      const float PA = s_PA[wave][lo + k], PB = s_PB[wave][lo + k];
+      if (gs >= 0)
+        *reinterpret_cast<float2*>(part + 2 * (grid_elem(gi) + k)) = make_float2(gA[k] * PA, gA[k] * PB + gB[k]);
+      if (ls >= 0) { lA[k] = qA[k] * PA; lB[k] = qA[k] * PB + qB[k]; }
+    }
+  }
+
+  // ---- the segment's carry-in: look-back over earlier segments of the slab
+  __shared__ float s_cin[SC];
+  if (tid < SC) {
+    const int cl = tid;
+    const int64_t widx = ((int64_t)seg * a.n_slabs + slab) * SC + cl;
+    float carry = 0.f;
+    if (seg == 0) {
+      const int chg = cs * SC + cl;
+      const int hh = chg / a.Dh;
+      carry = tn.h0 ? tn.h0[((int64_t)b * a.H + hh) * a.Dh + (chg - hh * a.Dh)] : 0.f;
+    } else {
+      publish(a.agg_a + widx, tag_word(segA, epoch));
+      publish(a.agg_b + widx, tag_word(segB, epoch));
+      float accA = 1.f, accB = 0.f;
+      int j = seg - 1;
+      uint32_t spins = 0;
+      bool done = false;
+      while (!done) {
+        const int64_t pidx = ((int64_t)j * a.n_slabs + slab) * SC + cl;
+        const uint64_t wi = peek(a.incl + pidx);
+        const uint64_t wa = peek(a.agg_a + pidx);
+        const uint64_t wb = peek(a.agg_b + pidx);
+        if (uint32_t(wi >> 32) == epoch) {
+          carry = accA * word_value(wi) + accB;
+          done = true;
+        } else if (uint32_t(wa >> 32) == epoch && uint32_t(wb >> 32) == epoch) {
+          accB = accA * word_value(wb) + accB;
+          accA *= word_value(wa);
+          --j;
+          spins = 0;
+        } else if (++spins > fallback_spins) {
+          // segment j shows no progress: fold its chunks in from the inputs
+          const int chg = cs * SC + cl;
+          float Aj = 1.f, Bj = 0.f;
+          for (int cj = j * a.seg_chunks; cj < min(n_chunks, (j + 1) * a.seg_chunks); ++cj) {
+            float Ac, Bc;
+            chunk_aggregate<XT, false>(static_cast<const XT*>(tn.x) + (int64_t)b * T * C + chg,
+                                       tn.z + (int64_t)b * T * C + chg, C, T, cj, a.p0, 0, Ac, Bc);
+            Bj = Ac * Bj + Bc;
+            Aj *= Ac;
+          }
+          accB = accA * Bj + accB;
+          accA *= Aj;
+          if (j == 0) {
+            const int hh = chg / a.Dh;
+            const float h0v = tn.h0 ? tn.h0[((int64_t)b * a.H + hh) * a.Dh + (chg - hh * a.Dh)] : 0.f;
+            carry = accA * h0v + accB;
+            done = true;
+          }
+          --j;
+          spins = 0;
+        } else {
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+    }
+    publish(a.incl + widx, tag_word(segA * carry + segB, epoch));
+    s_cin[cl] = carry;
+  }
+  __syncthreads();
+
+  // ---- phase B: grid states (and h_last) from the carry-in
+  float cin[NC];
+#pragma unroll
+  for (int k = 0; k < NC; ++k) cin[k] = s_cin[lo + k];
+  for (int c = c_begin; c < c_end; ++c) {
+    const int t0 = c * kChunkT + wave * kLW;
+    int gs;
+    int64_t gi;
+    grid_at(t0, gs, gi);
+    if (gs < 0) continue;
+    const int64_t e = grid_elem(gi);
+    float hv[NC];
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      const float2 ab = *reinterpret_cast<const float2*>(part + 2 * (e + k));
+      hv[k] = ab.x * cin[k] + ab.y;
+    }
+    if (tn.grid_mode == kGridHeadCol) {
+      const int64_t row = grid_row_offset(a.heads, a.B, b, h, 0, a.Dh) + (int64_t)d * a.heads.gcap[h];
+#pragma unroll
+      for (int k = 0; k < NC; ++k) store1(out_grid + row + (int64_t)k * a.heads.gcap[h] + col_key_pos(gi, d + k), hv[k]);
+    } else {
+      V::store(out_grid + e, hv);
+    }
+  }
+  // the wave holding position T-1
+  if (c_end == n_chunks && wave == ((T - 1) % kChunkT) / kLW) {
+    if (tn.h_last) {
+#pragma unroll
+      for (int k = 0; k < NC; ++k) tn.h_last[((int64_t)b * a.H + h) * a.Dh + d + k] = lA[k] * cin[k] + lB[k];
+    }
+    // the column grid past its last entry is zero
+    if (out_grid && tn.grid_mode == kGridHeadCol) {
+      const int cap = a.heads.gcap[h];
+      const int64_t row = grid_row_offset(a.heads, a.B, b, h, 0, a.Dh) + (int64_t)d * cap;
+      for (int64_t i = (a.p0 + T) / D; i < cap; ++i) {
+#pragma unroll
+        for (int k = 0; k < NC; ++k) store1(out_grid + row + (int64_t)k * cap + col_key_pos(i, d + k), 0.f);
+      }
+    }
+  }
+}
+
+// Blocks of `fn` (kNW waves each) that fit on the current device at once.
+int resident_blocks(const void* fn) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kNW * 64, 0) != hipSuccess)
+    return 0;
+  return cus * per_cu;
+}
+
+// Grid states only: no tensor stores every state, no restart, every stored
+// grid has D >= kLW.
+bool grid_only(const ScanTensor* ten, int ntensors, int reset_every, int H, const HeadTable& heads) {
+  if (reset_every > 0) return false;
+  for (int t = 0; t < ntensors; ++t) {
+    if (ten[t].out_all) return false;
+    if (!ten[t].out_grid) continue;
+    if (ten[t].grid_mode == kGridToken) {
+      if (heads.dil[0] < kLW) return false;
+    } else {
+      for (int h = 0; h < H; ++h)
+        if (heads.gcap[h] > 0 && heads.dil[h] < kLW) return false;
+    }
+  }
+  return true;
+}
+
+// Segments per slab: as many as fill the device once with every slab's
+// segments resident together, each at least one chunk.
+template <typename XT, int NC>
+hipError_t launch_segmented(ScanArgs a, int n_chunks, hipStream_t s) {
+  const int resident = resident_blocks(reinterpret_cast<const void*>(&scan_seg_kernel<XT, NC>));
+  if (resident <= 0) return hipErrorInvalidDevice;
+  int n_seg = resident / a.n_slabs;
+  n_seg = n_seg < 1 ? 1 : n_seg > n_chunks ? n_chunks : n_seg;
+  a.seg_chunks = (n_chunks + n_seg - 1) / n_seg;
+  a.n_seg = (n_chunks + a.seg_chunks - 1) / a.seg_chunks;   // no empty segment
+  hipLaunchKernelGGL((scan_seg_kernel<XT, NC>), dim3(a.n_seg * a.n_slabs), dim3(kNW * 64), 0, s, a);
+  return hipGetLastError();
+}
+
 template <typename XT, int NC>
 hipError_t launch_typed(const ScanArgs& a, int n_chunks, hipStream_t s) {
   const int blocks = n_chunks * a.n_slabs;
@@ -566,6 +887,8 @@ int pick_nc(int C) {
 
 }  // namespace
 
+bool scan_grid_only(const ScanPlan& p) { return grid_only(p.ten, p.ntensors, p.reset_every, p.H, p.heads); }
+
 size_t scan_workspace_bytes(int ntensors, int B, int T, int H, int Dh) {
   const int64_t C = (int64_t)H * Dh;
   const int64_t n_chunks = (T + kChunkT - 1) / kChunkT;
@@ -576,6 +899,8 @@ size_t scan_workspace_bytes(int ntensors, int B, int T, int H, int Dh) {
 hipError_t launch_scan(const ScanPlan& p, hipStream_t s) {
   if (p.T <= 0 || p.B <= 0) return hipSuccess;
   ScanArgs a;
+  a.part[0] = a.part[1] = nullptr;
+  a.n_seg = a.seg_chunks = 0;
   a.ten[0] = p.ten[0];
   a.ten[1] = p.ntensors > 1 ? p.ten[1] : p.ten[0];
   a.B = p.B; a.T = p.T; a.H = p.H; a.Dh = p.Dh; a.C = p.H * p.Dh;
@@ -600,6 +925,12 @@ hipError_t launch_scan(const ScanPlan& p, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nch = int(n_chunks);
+  if (p.part[0] && scan_grid_only(p)) {
+    a.part[0] = p.part[0];
+    a.part[1] = p.ntensors > 1 ? p.part[1] : p.part[0];
+    if (p.bf16) return nc == 2 ? launch_segmented<bf16_t, 2>(a, nch, s) : launch_segmented<bf16_t, 1>(a, nch, s);
+    return nc == 2 ? launch_segmented<float, 2>(a, nch, s) : launch_segmented<float, 1>(a, nch, s);
+  }
   if (p.bf16) return nc == 2 ? launch_typed<bf16_t, 2>(a, nch, s) : launch_typed<bf16_t, 1>(a, nch, s);
   return nc == 2 ? launch_typed<float, 2>(a, nch, s) : launch_typed<float, 1>(a, nch, s);
 }

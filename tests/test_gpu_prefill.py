@@ -41,7 +41,7 @@ def test_bf16_small(D, W):
     assert err <= BF16_TOL
 
 
-@pytest.mark.parametrize("D,W", [(2, 0), (8, 4), (1, 0)])
+@pytest.mark.parametrize("D,W", [(2, 0), (8, 4), (1, 0), (16, 0), (40, 0)])
 def test_fp32_small(D, W):
     x = inputs.prefill_inputs(2, 333, 2, 128, dtype=torch.float32, seed=D * 7 + W)
     out = _gpu(x, D, W)
@@ -54,6 +54,19 @@ def test_bf16_dh64_batch():
     out = _gpu(x, 4, 16)
     err = report("bf16 Dh=64 B=3", f64(out), _ref(x, 4, 16))
     assert err <= BF16_TOL
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("T", [64, 3000])
+def test_segmented_scan_prefill(dtype, T):
+    """No window and every D >= 16: the recurrence runs as the segmented
+    scan (grid states from per-segment (A, B) pairs).  Per-head D (16, 17,
+    64, 100, 1000), Dh = 64 (64-channel slabs), B = 2, ragged T."""
+    dil = [16, 17, 64, 100, 1000]
+    x = inputs.prefill_inputs(2, T, 5, 64, dtype=dtype, seed=T + 5)
+    out = _gpu(x, dil, 0)
+    err = report(f"segmented scan {dtype} T={T}", f64(out), _ref(x, dil, 0))
+    assert err <= (F32_TOL if dtype == torch.float32 else BF16_TOL)
 
 
 def test_per_head_dilation():
@@ -101,7 +114,8 @@ def _onehot_inputs(T, H, Dh, dtype, hot, seed):
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
 @pytest.mark.parametrize("D,W,hot", [(4, 0, 63), (4, 0, 64), (4, 0, 67), (16, 8, 47), (16, 8, 95),
                                      (16, 8, 96), (3, 5, 100), (8, 0, 7), (1, 0, 128), (1, 8, 100),
-                                     (1, 8, 200), (1, 70, 130)])
+                                     (1, 8, 200), (1, 70, 130), (16, 0, 47), (16, 0, 48), (64, 0, 127),
+                                     (64, 0, 191)])
 def test_key_set_boundaries_onehot(dtype, D, W, hot):
     T, H, Dh = 256, 2, 128
     x = _onehot_inputs(T, H, Dh, dtype, hot, seed=hot)

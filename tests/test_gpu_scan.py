@@ -57,6 +57,37 @@ def test_scan_shapes(dtype, H, Dh, E):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("H,Dh", [(1, 64), (3, 64), (2, 128)])
+@pytest.mark.parametrize("E", [16, 37, 64])
+def test_scan_grid_only_shapes(dtype, H, Dh, E):
+    """Grid states only, every E >= 16 (the persistent grid-only scan): at
+    most one stored state per 16 steps, taken from a partial aggregate;
+    ragged T, an initial state and the final state."""
+    B, T = 2, 1000
+    states, h_last, ref = _run(B, T, H, Dh, dtype, E, seed=H * 100 + E)
+    _check_states(states, ref, E, dtype, f"grid-only scan {dtype} H={H} Dh={Dh} E={E}")
+    assert np.max(np.abs(f64(h_last) - ref[:, -1])) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_scan_grid_only_long(dtype):
+    """Thousands of chunks per slab on persistent blocks (several items per
+    block), grid states every 64 steps."""
+    B, T, H, Dh = 1, 70000, 4, 128
+    states, h_last, ref = _run(B, T, H, Dh, dtype, 64, mu=4.0, seed=12)
+    _check_states(states, ref, 64, dtype, f"grid-only scan long {dtype}")
+    assert np.max(np.abs(f64(h_last) - ref[:, -1])) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_scan_grid_only_recompute_path(dtype):
+    """The grid-only scan with the look-back's local recompute on every wait."""
+    states, h_last, ref = _run(2, 5000, 2, 128, dtype, 32, seed=43, polls=0)
+    _check_states(states, ref, 32, dtype, f"grid-only scan fallback {dtype}")
+    assert np.max(np.abs(f64(h_last) - ref[:, -1])) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
 def test_scan_long_lookback(dtype):
     """Thousands of chunks: the carry crosses many look-back hops."""
     R = need_gpu()
@@ -160,8 +191,9 @@ def test_scan_lookback_recompute_path(dtype):
     assert np.max(np.abs(f64(h_last) - ref[:, -1])) <= 1e-5
 
 
-@pytest.mark.parametrize("dil,W", [(16, 32), (16, 0), ([1, 3, 32, 33], 0), ([2, 16, 1, 64], 8)],
-                         ids=["D16-W32", "D16-W0", "mixed-W0", "mixed-W8"])
+@pytest.mark.parametrize("dil,W", [(16, 32), (16, 0), ([1, 3, 32, 33], 0), ([2, 16, 1, 64], 8),
+                                   ([16, 33, 64, 100], 0)],
+                         ids=["D16-W32", "D16-W0", "mixed-W0", "mixed-W8", "grid-only-W0"])
 def test_prefill_with_lookback_recompute_path(dil, W):
     """The recompute fallback on every wait, with the grid layouts the scan
     writes from its LDS staging (dense heads, 2 <= D <= 32) and directly
