@@ -619,13 +619,16 @@ __global__ __launch_bounds__(kNW * 64) void scan_seg_kernel(const ScanArgs a) {
   const int D = tn.grid_mode == kGridToken ? a.heads.dil[0] : a.heads.dil[h];
   const int c_begin = seg * a.seg_chunks;
   const int c_end = min(n_chunks, c_begin + a.seg_chunks);
-  XT* const out_grid = tn.grid_mode != kGridToken && a.heads.gcap[h] == 0 ? nullptr
-                                                                          : static_cast<XT*>(tn.out_grid);
   const int64_t G_tok = T / D;
+  // per-lane table lookups taken once (inside the loops a memory clobber
+  // would reload them, and a vector load there waits for the inputs in flight)
+  const int gcap = a.heads.gcap[h];
+  XT* const out_grid = tn.grid_mode != kGridToken && gcap == 0 ? nullptr : static_cast<XT*>(tn.out_grid);
+  const int64_t grow0 = tn.grid_mode == kGridToken ? 0 : grid_row_offset(a.heads, a.B, b, h, 0, a.Dh);
   // element index of grid entry i of this lane's first channel (row-major)
   auto grid_elem = [&](int64_t i) __attribute__((always_inline)) -> int64_t {
     return tn.grid_mode == kGridToken ? (((int64_t)b * G_tok + i) * a.H + h) * a.Dh + d
-                                      : grid_row_offset(a.heads, a.B, b, h, i, a.Dh) + d;
+                                      : grow0 + i * a.Dh + d;
   };
   // the grid position in the kLW steps from row t0, as (step offset or -1, entry)
   auto grid_at = [&](int t0, int& gs, int64_t& gi) __attribute__((always_inline)) {
@@ -641,20 +644,14 @@ __global__ __launch_bounds__(kNW * 64) void scan_seg_kernel(const ScanArgs a) {
   const float* zbase = tn.z + (int64_t)b * T * C + cs * SC;
   typename V::raw xr[kLW];
   typename Z::raw zr[kLW];
-  // this wave's kLW steps of chunk c (c >= n_chunks: nothing is read)
-  auto load = [&](int c) __attribute__((always_inline)) {
-    const int t0 = c * kChunkT + wave * kLW;
-#pragma unroll
-    for (int s = 0; s < kLW; ++s) {
-      const int t = t0 + s;
-      if (t < T) {
-        xr[s] = V::load(xbase + (int64_t)t * C + lo);
-        zr[s] = Z::load(zbase + (int64_t)t * C + lo);
-      } else {
-        xr[s] = V::zero();
-        zr[s] = Z::zero();
-      }
-    }
+  // step s of this wave's kLW steps from row t0.  Rows past T read row T-1
+  // (pass 1 leaves such steps out): no branch around the loads, so the
+  // compiler's wait counts stay exact and the loads of the next chunk stay
+  // in flight under the current one.
+  auto load_step = [&](int t0, int s) __attribute__((always_inline)) {
+    const int t = min(t0 + s, T - 1);
+    xr[s] = V::load(xbase + (int64_t)t * C + lo);
+    zr[s] = Z::load(zbase + (int64_t)t * C + lo);
   };
 
   // ---- phase A
@@ -662,9 +659,14 @@ __global__ __launch_bounds__(kNW * 64) void scan_seg_kernel(const ScanArgs a) {
   float lA[NC], lB[NC];                    // the lane holding T-1: its aggregate from the segment start
 #pragma unroll
   for (int c = 0; c < NC; ++c) { lA[c] = 1.f; lB[c] = 0.f; }
-  load(c_begin);
+#pragma unroll
+  for (int s = 0; s < kLW; ++s) load_step(c_begin * kChunkT + wave * kLW, s);
   for (int c = c_begin; c < c_end; ++c) {
     const int t0 = c * kChunkT + wave * kLW;
+    // rows of the next chunk, loaded step by step into the registers pass 1
+    // has just consumed, so that a chunk's worth of loads is always in
+    // flight (past the segment's last chunk: rows past T, nothing read)
+    const int t0n = (c + 1 < c_end ? c + 1 : n_chunks) * kChunkT + wave * kLW;
     int gs;
     int64_t gi;
     grid_at(t0, gs, gi);
@@ -672,16 +674,19 @@ __global__ __launch_bounds__(kNW * 64) void scan_seg_kernel(const ScanArgs a) {
     float hl[NC], pp[NC], gA[NC], gB[NC], qA[NC], qB[NC];
 #pragma unroll
     for (int k = 0; k < NC; ++k) { hl[k] = 0.f; pp[k] = 1.f; gA[k] = qA[k] = 1.f; gB[k] = qB[k] = 0.f; }
+    V::hide(xr[0]);
+    Z::hide(zr[0]);
 #pragma unroll
     for (int s = 0; s < kLW; ++s) {
       const bool live = (t0 + s) < T;
 #pragma unroll
       for (int k = 0; k < NC; ++k) {
-        float cc = gate_comp(Z::get(zr[s], k));
-        float g = 1.f - cc;
-        if (!live) { g = 1.f; cc = 0.f; }
-        hl[k] = g * hl[k] + cc * V::get(xr[s], k);
-        pp[k] *= g;
+        const float cc = gate_comp(Z::get(zr[s], k));
+        const float g = 1.f - cc;
+        const float hn = g * hl[k] + cc * V::get(xr[s], k);
+        const float pn = pp[k] * g;
+        hl[k] = live ? hn : hl[k];   // a step past T (a repeated row) leaves the state alone
+        pp[k] = live ? pn : pp[k];
         gA[k] = s == gs ? pp[k] : gA[k];
         gB[k] = s == gs ? hl[k] : gB[k];
         qA[k] = s == ls ? pp[k] : qA[k];
@@ -690,12 +695,17 @@ __global__ __launch_bounds__(kNW * 64) void scan_seg_kernel(const ScanArgs a) {
         // for a selection at the end)
         opaque(gA[k]); opaque(gB[k]); opaque(qA[k]); opaque(qB[k]);
       }
+      asm volatile("" ::: "memory");   // the reload stays after this step's use
+      load_step(t0n, s);
+      // step s + 1 is used only from here on (else the compiler hoists its
+      // arithmetic above the reloads and waits for the whole chunk at once)
+      if (s + 1 < kLW) {
+        V::hide(xr[s + 1]);
+        Z::hide(zr[s + 1]);
+      }
     }
 #pragma unroll
     for (int k = 0; k < NC; ++k) { s_A[wave][lo + k] = pp[k]; s_B[wave][lo + k] = hl[k]; }
-    // the next chunk's inputs land while this one is folded (past the
-    // segment's last chunk: a chunk index past the sequence, nothing read)
-    load(c + 1 < c_end ? c + 1 : n_chunks);
     __syncthreads();
     if (tid < SC) {
       float pA = segA, pB = segB;
@@ -799,9 +809,9 @@ __global__ __launch_bounds__(kNW * 64) void scan_seg_kernel(const ScanArgs a) {
       hv[k] = ab.x * cin[k] + ab.y;
     }
     if (tn.grid_mode == kGridHeadCol) {
-      const int64_t row = grid_row_offset(a.heads, a.B, b, h, 0, a.Dh) + (int64_t)d * a.heads.gcap[h];
+      const int64_t row = grow0 + (int64_t)d * gcap;
 #pragma unroll
-      for (int k = 0; k < NC; ++k) store1(out_grid + row + (int64_t)k * a.heads.gcap[h] + col_key_pos(gi, d + k), hv[k]);
+      for (int k = 0; k < NC; ++k) store1(out_grid + row + (int64_t)k * gcap + col_key_pos(gi, d + k), hv[k]);
     } else {
       V::store(out_grid + e, hv);
     }
@@ -814,8 +824,8 @@ __global__ __launch_bounds__(kNW * 64) void scan_seg_kernel(const ScanArgs a) {
     }
     // the column grid past its last entry is zero
     if (out_grid && tn.grid_mode == kGridHeadCol) {
-      const int cap = a.heads.gcap[h];
-      const int64_t row = grid_row_offset(a.heads, a.B, b, h, 0, a.Dh) + (int64_t)d * cap;
+      const int cap = gcap;
+      const int64_t row = grow0 + (int64_t)d * cap;
       for (int64_t i = (a.p0 + T) / D; i < cap; ++i) {
 #pragma unroll
         for (int k = 0; k < NC; ++k) store1(out_grid + row + (int64_t)k * cap + col_key_pos(i, d + k), 0.f);
