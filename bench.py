@@ -597,11 +597,17 @@ def measure_copy(torch):
 # offline: rocprofv3 CSV output -> short summaries under profiles/ (CPU only)
 # ---------------------------------------------------------------------------
 
-KERNEL_PATTERNS = {"scan": "scan_kernel", "attention": "attn_bf16_kernel", "decode": "decode_kernel",
+KERNEL_PATTERNS = {"scan": ("scan_kernel", "scan_seg_kernel"), "attention": "attn_bf16_kernel",
+                   "decode": "decode_kernel",
                    "topk_attend": "topk_attend_kernel", "topk_stats": "topk_stats_kernel",
                    "topk_append": "topk_append_kernel", "grid_to_col": "grid_to_col_kernel",
                    "ring_prefix": "ring_prefix_kernel", "topk_select": "topk_select_tile_kernel"}
 COPY_BYTES = 1 << 30   # --calibrate-copy: bytes read and bytes written by one copy
+
+
+def _matches(name, pat):
+    """Whether a kernel name holds the pattern (or one of a tuple of them)."""
+    return any(p in name for p in ((pat,) if isinstance(pat, str) else pat))
 
 
 def _find_csv(d, suffix):
@@ -627,8 +633,8 @@ def summarize_pmc(kernel, workload, fetch_dir, write_dir, cfetch_dir, cwrite_dir
     the same counters read for a plain copy of known size, into
     profiles/<kernel>_<workload>_pmc.json (+ .txt)."""
     pat = KERNEL_PATTERNS[kernel]
-    fetch = [v for n, v in _counter_rows(fetch_dir, "FETCH_SIZE") if pat in n]
-    write = [v for n, v in _counter_rows(write_dir, "WRITE_SIZE") if pat in n]
+    fetch = [v for n, v in _counter_rows(fetch_dir, "FETCH_SIZE") if _matches(n, pat)]
+    write = [v for n, v in _counter_rows(write_dir, "WRITE_SIZE") if _matches(n, pat)]
     # the calibration run's largest dispatch is the 1 GiB copy
     cf = max(v for _, v in _counter_rows(cfetch_dir, "FETCH_SIZE"))
     cw = max(v for _, v in _counter_rows(cwrite_dir, "WRITE_SIZE"))
@@ -669,7 +675,7 @@ def summarize_trace(trace_dir, kernel, workload, bench_args):
     path = _find_csv(trace_dir, "kernel_stats.csv")
     pat = KERNEL_PATTERNS[kernel]
     with open(path) as fh:
-        rows = [r for r in csv.DictReader(fh) if pat in r["Name"]]
+        rows = [r for r in csv.DictReader(fh) if _matches(r["Name"], pat)]
     lines = [f"rocprofv3 kernel statistics of {kernel} ({pat}) on workload {workload}", "",
              f"$ rocprofv3 --kernel-trace --stats --output-format csv -d {trace_dir} -o kt -- python3 bench.py "
              f"{bench_args}",
@@ -679,7 +685,7 @@ def summarize_trace(trace_dir, kernel, workload, bench_args):
     # the first three (cold) dispatches, next to the --stats figures
     import statistics
     with open(_find_csv(trace_dir, "kernel_trace.csv")) as fh:
-        trace = [r for r in csv.DictReader(fh) if pat in r["Kernel_Name"]]
+        trace = [r for r in csv.DictReader(fh) if _matches(r["Kernel_Name"], pat)]
     for r in rows:
         ds = [(int(t["End_Timestamp"]) - int(t["Start_Timestamp"])) / 1e3 for t in trace
               if t["Kernel_Name"] == r["Name"]]
