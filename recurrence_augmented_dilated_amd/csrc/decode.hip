@@ -156,8 +156,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(const DecArgs a) {
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t r = base + u * KPW + rg;
       const bool ok = r < w_hi;
-      kr[u] = ok ? R::load(gk + r * DH) : R::zero();
-      vr[u] = ok ? R::load(gv + r * DH) : R::zero();
+      kr[u] = ok ? R::load_nt(gk + r * DH) : R::zero();
+      vr[u] = ok ? R::load_nt(gv + r * DH) : R::zero();
     }
     float sc[kUnroll];
     float vv[kUnroll][8];

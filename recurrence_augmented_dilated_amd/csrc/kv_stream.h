@@ -13,6 +13,13 @@ template <typename ET> struct Row8;
 template <> struct Row8<bf16_t> {
   using raw = uint4;
   __device__ static raw load(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+  // a row read once per call (the cache streams): non-temporal, so that it
+  // does not displace reused data from the caches
+  __device__ static raw load_nt(const bf16_t* p) {
+    typedef unsigned u4_t __attribute__((ext_vector_type(4)));
+    const u4_t v = __builtin_nontemporal_load(reinterpret_cast<const u4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  }
   __device__ static raw zero() { return make_uint4(0, 0, 0, 0); }
   __device__ static void get(const raw& r, float* f) {
     f[0] = bf16_lo(r.x); f[1] = bf16_hi(r.x); f[2] = bf16_lo(r.y); f[3] = bf16_hi(r.y);
@@ -29,6 +36,12 @@ template <> struct Row8<float> {
   struct raw { float4 a, b; };
   __device__ static raw load(const float* p) {
     return raw{reinterpret_cast<const float4*>(p)[0], reinterpret_cast<const float4*>(p)[1]};
+  }
+  __device__ static raw load_nt(const float* p) {
+    typedef float f4_t __attribute__((ext_vector_type(4)));
+    const f4_t a = __builtin_nontemporal_load(reinterpret_cast<const f4_t*>(p));
+    const f4_t b = __builtin_nontemporal_load(reinterpret_cast<const f4_t*>(p) + 1);
+    return raw{make_float4(a.x, a.y, a.z, a.w), make_float4(b.x, b.y, b.z, b.w)};
   }
   __device__ static raw zero() { return raw{make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)}; }
   __device__ static void get(const raw& r, float* f) {

@@ -45,14 +45,14 @@ __device__ __forceinline__ void gate_pair(float z, float& g, float& c) {
   g = pos ? big : small;
   c = pos ? small : big;
 }
-// sigmoid(-z) = 1 - g by itself, the input weight of the recurrence.  The
-// prefill scan keeps only this value per element and takes the decay as one
-// minus it: one rounding, an absolute error near 1e-7 that is relatively
-// large only where the decay itself is negligible.
+// sigmoid(-z) = 1 - g by itself, the input weight of the recurrence, as
+// 1 / (1 + e^z) (e^z overflowing to inf gives 0, z = -inf gives exactly 1,
+// NaN propagates).  Its relative error is that of e^z taken as
+// 2^(z log2 e): about |z| ulps from rounding the exponent, a few ulps where
+// the value matters.  The prefill scan keeps only this value per element and
+// applies the decay as h - c h, with no rounded 1 - c.
 __device__ __forceinline__ float gate_comp(float z) {
-  const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * fabsf(z));
-  const float big = __builtin_amdgcn_rcpf(1.0f + e);
-  return z >= 0.0f ? e * big : big;
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(1.4426950408889634f * z));
 }
 
 // ---------------------------------------------------------------------------

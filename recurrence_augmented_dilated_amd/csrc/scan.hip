@@ -40,6 +40,10 @@ namespace {
 constexpr int kLW = 16;              // time steps per wave
 constexpr int kNW = 8;               // waves per block
 constexpr int kChunkT = kLW * kNW;   // time steps per block
+constexpr int kSegNW = 16;           // waves per segmented-scan block (one block per CU: no
+                                     // wave-age skew between two resident blocks)
+constexpr int kSegChunkT = kLW * kSegNW;   // time steps per segmented-scan chunk
+static_assert(kSegChunkT % kChunkT == 0, "a segment chunk is whole plain chunks");
 static_assert(kSegMinD >= kLW, "a grid-only wave holds at most one grid position");
 constexpr int kWin = 2;              // predecessors read per look-back round trip
 constexpr int kSparseMaxD = 32;      // largest D whose column grid is staged through LDS
@@ -56,6 +60,9 @@ template <typename XT, int NC> struct XVec;
 template <> struct XVec<bf16_t, 2> {
   using raw = uint32_t;
   __device__ static raw load(const bf16_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+  __device__ static raw load_nt(const bf16_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+  }
   __device__ static float get(const raw& r, int c) { return c ? bf16_hi(r) : bf16_lo(r); }
   __device__ static void store(bf16_t* p, const float* v) {
     *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(v[0], v[1]);
@@ -66,6 +73,7 @@ template <> struct XVec<bf16_t, 2> {
 template <> struct XVec<bf16_t, 1> {
   using raw = uint32_t;
   __device__ static raw load(const bf16_t* p) { return uint32_t(*p); }
+  __device__ static raw load_nt(const bf16_t* p) { return uint32_t(__builtin_nontemporal_load(p)); }
   __device__ static float get(const raw& r, int) { return bf16_lo(r); }
   __device__ static void store(bf16_t* p, const float* v) {
     *p = bf16_t(pack_bf16x2(v[0], 0.f) & 0xffffu);
@@ -76,6 +84,11 @@ template <> struct XVec<bf16_t, 1> {
 template <> struct XVec<float, 2> {
   using raw = float2;
   __device__ static raw load(const float* p) { return *reinterpret_cast<const float2*>(p); }
+  __device__ static raw load_nt(const float* p) {
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+    const f2_t v = __builtin_nontemporal_load(reinterpret_cast<const f2_t*>(p));
+    return make_float2(v.x, v.y);
+  }
   __device__ static float get(const raw& r, int c) { return c ? r.y : r.x; }
   __device__ static void store(float* p, const float* v) {
     *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
@@ -87,6 +100,7 @@ template <> struct XVec<float, 2> {
 template <> struct XVec<float, 1> {
   using raw = float;
   __device__ static raw load(const float* p) { return *p; }
+  __device__ static raw load_nt(const float* p) { return __builtin_nontemporal_load(p); }
   __device__ static float get(const raw& r, int) { return r; }
   __device__ static void store(float* p, const float* v) { *p = v[0]; }
   __device__ static raw zero() { return 0.f; }
@@ -296,19 +310,17 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
   const float* zbase = tn.z + (int64_t)b * T * C + cs * SC;
   const int lo = lane * NC;
 
-  // ---- load this wave's kLW steps (every element is read exactly once)
+  // ---- load this wave's kLW steps (every element is read exactly once, as
+  // a stream: non-temporal).  Rows past T read row T-1, which the passes
+  // leave out: no branch around a load, so that no arithmetic lands between
+  // the loads with a wait for each.
   typename V::raw xr[kLW];
   typename Z::raw zr[kLW];
 #pragma unroll
   for (int s = 0; s < kLW; ++s) {
-    const int t = t0 + s;
-    if (t < T) {
-      xr[s] = V::load(xbase + (int64_t)t * C + lo);
-      zr[s] = Z::load(zbase + (int64_t)t * C + lo);
-    } else {
-      xr[s] = V::zero();
-      zr[s] = Z::zero();
-    }
+    const int t = min(t0 + s, T - 1);
+    xr[s] = V::load_nt(xbase + (int64_t)t * C + lo);
+    zr[s] = Z::load_nt(zbase + (int64_t)t * C + lo);
   }
 
   // first restart position >= p0 + t0 (chunk-local recurrence), or none
@@ -567,13 +579,16 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
 
 // Segmented scan for grid-only outputs (no all-state output, no restart,
 // every stored grid with D >= kLW, so a wave's kLW steps hold at most one
-// grid position).  Block = (segment, slab): a contiguous run of seg_chunks
-// chunks of one slab, walked in order with the next chunk's inputs in flight
-// while the current one is folded.  Phase A: per chunk, each wave folds its
-// steps into its aggregate and the partial aggregate up to its grid position;
-// one thread per channel keeps the segment's running aggregate and hands
-// every wave the aggregate from the segment start to the wave's first step,
-// so each grid position gets its (A, B) relative to the segment start,
+// grid position).  Block = (segment, slab), kSegNW waves, one block per CU:
+// a contiguous run of seg_chunks chunks of kSegChunkT steps of one slab,
+// walked in order with the next chunk's inputs in flight while the current
+// one is folded.  (Two 8-wave blocks per CU ran unevenly: the older block's
+// waves win the issue arbitration, and the younger block set the kernel's
+// time at ~1.33x the older one's.)  Phase A: per chunk, each wave folds its
+// steps into its aggregate and the partial aggregate up to its grid
+// position; one thread per channel keeps the segment's running aggregate and
+// hands every wave the aggregate from the segment start to the wave's first
+// step, so each grid position gets its (A, B) relative to the segment start,
 // written to part[] (state = A * carry_in + B).  The segment's aggregate then
 // goes through the same decoupled look-back as the chunked scan, over
 // segments instead of chunks (a handful per slab, all resident at once), and
@@ -581,15 +596,15 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
 // element is read once; part[] adds 8 bytes per grid element written and
 // read.
 template <typename XT, int NC>
-__global__ __launch_bounds__(kNW * 64) void scan_seg_kernel(const ScanArgs a) {
+__global__ __launch_bounds__(kSegNW * 64) void scan_seg_kernel(const ScanArgs a) {
   using V = XVec<XT, NC>;
   using Z = XVec<float, NC>;
   constexpr int SC = 64 * NC;   // channels per slab
-  static_assert(SC <= kNW * 64, "one prefix thread per channel");
-  __shared__ float s_A[kNW][SC];
-  __shared__ float s_B[kNW][SC];
-  __shared__ float s_PA[kNW][SC];   // aggregate from the segment start to each wave's first step
-  __shared__ float s_PB[kNW][SC];
+  static_assert(SC <= kSegNW * 64, "one prefix thread per channel");
+  __shared__ float s_A[kSegNW][SC];
+  __shared__ float s_B[kSegNW][SC];
+  __shared__ float s_PA[kSegNW][SC];   // aggregate from the segment start to each wave's first step
+  __shared__ float s_PB[kSegNW][SC];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -602,7 +617,7 @@ __global__ __launch_bounds__(kNW * 64) void scan_seg_kernel(const ScanArgs a) {
   const uint32_t fallback_spins = poll_word ? poll_word - 1u : kFallbackSpins * 256u;
   const int64_t C = a.C;
   const int T = a.T;
-  const int n_chunks = int(((int64_t)T + kChunkT - 1) / kChunkT);
+  const int n_chunks = int(((int64_t)T + kSegChunkT - 1) / kSegChunkT);
   const int seg = int(blockIdx.x) / a.n_slabs;
   const int slab = int(blockIdx.x) - seg * a.n_slabs;
   const int per_tensor = a.B * a.slabs_per_bt;
@@ -630,14 +645,32 @@ __global__ __launch_bounds__(kNW * 64) void scan_seg_kernel(const ScanArgs a) {
     return tn.grid_mode == kGridToken ? (((int64_t)b * G_tok + i) * a.H + h) * a.Dh + d
                                       : grow0 + i * a.Dh + d;
   };
-  // the grid position in the kLW steps from row t0, as (step offset or -1, entry)
-  auto grid_at = [&](int t0, int& gs, int64_t& gi) __attribute__((always_inline)) {
-    const int64_t ja0 = a.p0 + t0;
+  // the same entry's (A, B) pair in part[]: head-major in both layouts, so
+  // that a block's pairs fill one run of memory in entry order (pairs
+  // scattered over the token-major rows slow the input stream down)
+  auto part_elem = [&](int64_t i) __attribute__((always_inline)) -> int64_t {
+    return tn.grid_mode == kGridToken ? (((int64_t)b * a.H + h) * G_tok + i) * a.Dh + d
+                                      : grow0 + i * a.Dh + d;
+  };
+  // The next grid position at or after this wave's first step in phase A,
+  // tracked from chunk to chunk without divisions: r = its offset from the
+  // first step (in [0, D)), pe = its entry's pair index in part[].  A chunk
+  // moves the first step kSegChunkT = mq * D + mr rows on.
+  const int mq = kSegChunkT / D, mr = kSegChunkT - mq * D;
+  int r;
+  int64_t pe;
+  {
+    const int64_t ja0 = a.p0 + (int64_t)c_begin * kSegChunkT + wave * kLW;
     int64_t nxt = (ja0 / D) * D + (D - 1);
     if (nxt < ja0) nxt += D;
-    const int64_t off = nxt - ja0;
-    gs = (out_grid && off < kLW && t0 + off < T) ? int(off) : -1;
-    gi = (nxt + 1) / D - 1;
+    r = int(nxt - ja0);
+    pe = part_elem((nxt + 1) / D - 1);
+  }
+  auto advance = [&]() __attribute__((always_inline)) {
+    r -= mr;
+    const bool wrap = r < 0;
+    r += wrap ? D : 0;
+    pe += (int64_t)(mq + (wrap ? 1 : 0)) * a.Dh;
   };
 
   const XT* xbase = static_cast<const XT*>(tn.x) + (int64_t)b * T * C + cs * SC;
@@ -648,10 +681,13 @@ __global__ __launch_bounds__(kNW * 64) void scan_seg_kernel(const ScanArgs a) {
   // (pass 1 leaves such steps out): no branch around the loads, so the
   // compiler's wait counts stay exact and the loads of the next chunk stay
   // in flight under the current one.
+  // The inputs are read once, as a stream: non-temporal loads, which keep
+  // them from displacing the (A, B) pairs from the caches on their way to
+  // memory (with plain loads the scan runs ~9% slower on T = 262144).
   auto load_step = [&](int t0, int s) __attribute__((always_inline)) {
     const int t = min(t0 + s, T - 1);
-    xr[s] = V::load(xbase + (int64_t)t * C + lo);
-    zr[s] = Z::load(zbase + (int64_t)t * C + lo);
+    xr[s] = V::load_nt(xbase + (int64_t)t * C + lo);
+    zr[s] = Z::load_nt(zbase + (int64_t)t * C + lo);
   };
 
   // ---- phase A
@@ -659,18 +695,22 @@ __global__ __launch_bounds__(kNW * 64) void scan_seg_kernel(const ScanArgs a) {
   float lA[NC], lB[NC];                    // the lane holding T-1: its aggregate from the segment start
 #pragma unroll
   for (int c = 0; c < NC; ++c) { lA[c] = 1.f; lB[c] = 0.f; }
+  // the first chunk's rows in step order, as the loop reloads them (the wait
+  // for step 0 at the loop head is taken over both entries to the loop: out
+  // of order here, it would wait for the whole chunk on every iteration)
 #pragma unroll
-  for (int s = 0; s < kLW; ++s) load_step(c_begin * kChunkT + wave * kLW, s);
+  for (int s = 0; s < kLW; ++s) {
+    load_step(c_begin * kSegChunkT + wave * kLW, s);
+    asm volatile("" ::: "memory");
+  }
   for (int c = c_begin; c < c_end; ++c) {
-    const int t0 = c * kChunkT + wave * kLW;
+    const int t0 = c * kSegChunkT + wave * kLW;
     // rows of the next chunk, loaded step by step into the registers pass 1
     // has just consumed, so that a chunk's worth of loads is always in
     // flight (past the segment's last chunk: rows past T, nothing read)
-    const int t0n = (c + 1 < c_end ? c + 1 : n_chunks) * kChunkT + wave * kLW;
-    int gs;
-    int64_t gi;
-    grid_at(t0, gs, gi);
-    const int ls = (tn.h_last && t0 <= T - 1 && T - 1 < t0 + kLW) ? T - 1 - t0 : -1;
+    const int t0n = (c + 1 < c_end ? c + 1 : n_chunks) * kSegChunkT + wave * kLW;
+    const int gs = (out_grid && r < kLW && t0 + r < T) ? r : -1;
+    const int ls = (tn.h_last && t0 <= T - 1 && T - 1 < t0 + kLW) ? T - 1 - t0 : -1;   // uniform
     float hl[NC], pp[NC], gA[NC], gB[NC], qA[NC], qB[NC];
 #pragma unroll
     for (int k = 0; k < NC; ++k) { hl[k] = 0.f; pp[k] = 1.f; gA[k] = qA[k] = 1.f; gB[k] = qB[k] = 0.f; }
@@ -678,22 +718,23 @@ __global__ __launch_bounds__(kNW * 64) void scan_seg_kernel(const ScanArgs a) {
     Z::hide(zr[0]);
 #pragma unroll
     for (int s = 0; s < kLW; ++s) {
-      const bool live = (t0 + s) < T;
+      // Steps past T (repeated rows in the last chunk) are folded in too:
+      // what follows T-1 reaches no stored value (no grid position or h_last
+      // lies past it, and no later segment or wave reads the aggregates).
 #pragma unroll
       for (int k = 0; k < NC; ++k) {
         const float cc = gate_comp(Z::get(zr[s], k));
-        const float g = 1.f - cc;
-        const float hn = g * hl[k] + cc * V::get(xr[s], k);
-        const float pn = pp[k] * g;
-        hl[k] = live ? hn : hl[k];   // a step past T (a repeated row) leaves the state alone
-        pp[k] = live ? pn : pp[k];
+        hl[k] = fmaf(cc, V::get(xr[s], k), fmaf(-cc, hl[k], hl[k]));   // (1 - c) h + c x
+        pp[k] = fmaf(-pp[k], cc, pp[k]);                                 // (1 - c) p
         gA[k] = s == gs ? pp[k] : gA[k];
         gB[k] = s == gs ? hl[k] : gB[k];
-        qA[k] = s == ls ? pp[k] : qA[k];
-        qB[k] = s == ls ? hl[k] : qB[k];
         // taken here, step by step (else every step's products stay live
         // for a selection at the end)
-        opaque(gA[k]); opaque(gB[k]); opaque(qA[k]); opaque(qB[k]);
+        opaque(gA[k]); opaque(gB[k]);
+      }
+      if (s == ls) {
+#pragma unroll
+        for (int k = 0; k < NC; ++k) { qA[k] = pp[k]; qB[k] = hl[k]; }
       }
       asm volatile("" ::: "memory");   // the reload stays after this step's use
       load_step(t0n, s);
@@ -710,7 +751,7 @@ __global__ __launch_bounds__(kNW * 64) void scan_seg_kernel(const ScanArgs a) {
     if (tid < SC) {
       float pA = segA, pB = segB;
 #pragma unroll
-      for (int w = 0; w < kNW; ++w) {
+      for (int w = 0; w < kSegNW; ++w) {
         s_PA[w][tid] = pA;
         s_PB[w][tid] = pB;
         const float Aw = s_A[w][tid];
@@ -725,9 +766,10 @@ __global__ __launch_bounds__(kNW * 64) void scan_seg_kernel(const ScanArgs a) {
     for (int k = 0; k < NC; ++k) {
       const float PA = s_PA[wave][lo + k], PB = s_PB[wave][lo + k];
       if (gs >= 0)
-        *reinterpret_cast<float2*>(part + 2 * (grid_elem(gi) + k)) = make_float2(gA[k] * PA, gA[k] * PB + gB[k]);
+        *reinterpret_cast<float2*>(part + 2 * (pe + k)) = make_float2(gA[k] * PA, gA[k] * PB + gB[k]);
       if (ls >= 0) { lA[k] = qA[k] * PA; lB[k] = qA[k] * PB + qB[k]; }
     }
+    advance();
   }
 
   // ---- the segment's carry-in: look-back over earlier segments of the slab
@@ -764,7 +806,9 @@ __global__ __launch_bounds__(kNW * 64) void scan_seg_kernel(const ScanArgs a) {
           // segment j shows no progress: fold its chunks in from the inputs
           const int chg = cs * SC + cl;
           float Aj = 1.f, Bj = 0.f;
-          for (int cj = j * a.seg_chunks; cj < min(n_chunks, (j + 1) * a.seg_chunks); ++cj) {
+          constexpr int per = kSegChunkT / kChunkT;   // plain chunks per segment chunk
+          const int nc_plain = int(((int64_t)T + kChunkT - 1) / kChunkT);
+          for (int cj = j * a.seg_chunks * per; cj < min(nc_plain, (j + 1) * a.seg_chunks * per); ++cj) {
             float Ac, Bc;
             chunk_aggregate<XT, false>(static_cast<const XT*>(tn.x) + (int64_t)b * T * C + chg,
                                        tn.z + (int64_t)b * T * C + chg, C, T, cj, a.p0, 0, Ac, Bc);
@@ -795,29 +839,43 @@ __global__ __launch_bounds__(kNW * 64) void scan_seg_kernel(const ScanArgs a) {
   float cin[NC];
 #pragma unroll
   for (int k = 0; k < NC; ++k) cin[k] = s_cin[lo + k];
-  for (int c = c_begin; c < c_end; ++c) {
-    const int t0 = c * kChunkT + wave * kLW;
-    int gs;
-    int64_t gi;
-    grid_at(t0, gs, gi);
-    if (gs < 0) continue;
-    const int64_t e = grid_elem(gi);
-    float hv[NC];
+  // The segment's entries are spread over the waves, kPB of them in flight
+  // per lane (each is a load, an FMA and a store).
+  if (out_grid) {
+    constexpr int kPB = 4;
+    const int64_t pos_lo = a.p0 + (int64_t)c_begin * kSegChunkT;
+    const int64_t pos_hi = a.p0 + min((int64_t)c_end * kSegChunkT, (int64_t)T);
+    const int64_t e_lo = (pos_lo + D) / D - 1;   // first entry at or after pos_lo
+    const int64_t e_hi = pos_hi / D;             // entries before pos_hi
+    const int64_t pe_lo = part_elem(e_lo);
+    for (int64_t e0 = e_lo + wave; e0 < e_hi; e0 += kSegNW * kPB) {
+      float2 ab[kPB][NC];
 #pragma unroll
-    for (int k = 0; k < NC; ++k) {
-      const float2 ab = *reinterpret_cast<const float2*>(part + 2 * (e + k));
-      hv[k] = ab.x * cin[k] + ab.y;
-    }
-    if (tn.grid_mode == kGridHeadCol) {
-      const int64_t row = grow0 + (int64_t)d * gcap;
+      for (int j = 0; j < kPB; ++j) {
+        const int64_t e = min(e0 + j * kSegNW, e_hi - 1);
+        const int64_t q = pe_lo + (e - e_lo) * a.Dh;
 #pragma unroll
-      for (int k = 0; k < NC; ++k) store1(out_grid + row + (int64_t)k * gcap + col_key_pos(gi, d + k), hv[k]);
-    } else {
-      V::store(out_grid + e, hv);
+        for (int k = 0; k < NC; ++k) ab[j][k] = *reinterpret_cast<const float2*>(part + 2 * (q + k));
+      }
+#pragma unroll
+      for (int j = 0; j < kPB; ++j) {
+        const int64_t e = e0 + j * kSegNW;
+        if (e >= e_hi) break;
+        float hv[NC];
+#pragma unroll
+        for (int k = 0; k < NC; ++k) hv[k] = ab[j][k].x * cin[k] + ab[j][k].y;
+        if (tn.grid_mode == kGridHeadCol) {
+          const int64_t row = grow0 + (int64_t)d * gcap;
+#pragma unroll
+          for (int k = 0; k < NC; ++k) store1(out_grid + row + (int64_t)k * gcap + col_key_pos(e, d + k), hv[k]);
+        } else {
+          V::store(out_grid + grid_elem(e), hv);
+        }
+      }
     }
   }
   // the wave holding position T-1
-  if (c_end == n_chunks && wave == ((T - 1) % kChunkT) / kLW) {
+  if (c_end == n_chunks && wave == ((T - 1) % kSegChunkT) / kLW) {
     if (tn.h_last) {
 #pragma unroll
       for (int k = 0; k < NC; ++k) tn.h_last[((int64_t)b * a.H + h) * a.Dh + d + k] = lA[k] * cin[k] + lB[k];
@@ -834,12 +892,12 @@ __global__ __launch_bounds__(kNW * 64) void scan_seg_kernel(const ScanArgs a) {
   }
 }
 
-// Blocks of `fn` (kNW waves each) that fit on the current device at once.
-int resident_blocks(const void* fn) {
+// Blocks of `fn` (`threads` each) that fit on the current device at once.
+int resident_blocks(const void* fn, int threads) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kNW * 64, 0) != hipSuccess)
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0) != hipSuccess)
     return 0;
   return cus * per_cu;
 }
@@ -864,14 +922,15 @@ bool grid_only(const ScanTensor* ten, int ntensors, int reset_every, int H, cons
 // Segments per slab: as many as fill the device once with every slab's
 // segments resident together, each at least one chunk.
 template <typename XT, int NC>
-hipError_t launch_segmented(ScanArgs a, int n_chunks, hipStream_t s) {
-  const int resident = resident_blocks(reinterpret_cast<const void*>(&scan_seg_kernel<XT, NC>));
+hipError_t launch_segmented(ScanArgs a, hipStream_t s) {
+  const int resident = resident_blocks(reinterpret_cast<const void*>(&scan_seg_kernel<XT, NC>), kSegNW * 64);
   if (resident <= 0) return hipErrorInvalidDevice;
+  const int n_chunks = int(((int64_t)a.T + kSegChunkT - 1) / kSegChunkT);
   int n_seg = resident / a.n_slabs;
   n_seg = n_seg < 1 ? 1 : n_seg > n_chunks ? n_chunks : n_seg;
   a.seg_chunks = (n_chunks + n_seg - 1) / n_seg;
   a.n_seg = (n_chunks + a.seg_chunks - 1) / a.seg_chunks;   // no empty segment
-  hipLaunchKernelGGL((scan_seg_kernel<XT, NC>), dim3(a.n_seg * a.n_slabs), dim3(kNW * 64), 0, s, a);
+  hipLaunchKernelGGL((scan_seg_kernel<XT, NC>), dim3(a.n_seg * a.n_slabs), dim3(kSegNW * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -938,8 +997,8 @@ hipError_t launch_scan(const ScanPlan& p, hipStream_t s) {
   if (p.part[0] && scan_grid_only(p)) {
     a.part[0] = p.part[0];
     a.part[1] = p.ntensors > 1 ? p.part[1] : p.part[0];
-    if (p.bf16) return nc == 2 ? launch_segmented<bf16_t, 2>(a, nch, s) : launch_segmented<bf16_t, 1>(a, nch, s);
-    return nc == 2 ? launch_segmented<float, 2>(a, nch, s) : launch_segmented<float, 1>(a, nch, s);
+    if (p.bf16) return nc == 2 ? launch_segmented<bf16_t, 2>(a, s) : launch_segmented<bf16_t, 1>(a, s);
+    return nc == 2 ? launch_segmented<float, 2>(a, s) : launch_segmented<float, 1>(a, s);
   }
   if (p.bf16) return nc == 2 ? launch_typed<bf16_t, 2>(a, nch, s) : launch_typed<bf16_t, 1>(a, nch, s);
   return nc == 2 ? launch_typed<float, 2>(a, nch, s) : launch_typed<float, 1>(a, nch, s);

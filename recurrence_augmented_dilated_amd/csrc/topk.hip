@@ -314,7 +314,9 @@ __global__ __launch_bounds__(kAW * 64) void topk_select_tile_kernel(const TopkPl
 constexpr int kRankMax = 1024;
 
 // ---- selection and attention: one workgroup per query
-template <typename ET, int DH>
+// STREAM (decode): every kept row is read by this one query only, so the rows
+// are read non-temporally; prefill queries share kept blocks through the cache.
+template <typename ET, int DH, bool STREAM>
 __global__ __launch_bounds__(kAW * 64) void topk_attend_kernel(const TopkPlan p) {
   using R = Row8<ET>;
   constexpr int LPK = DH / 8;      // lanes per row
@@ -489,8 +491,8 @@ __global__ __launch_bounds__(kAW * 64) void topk_attend_kernel(const TopkPlan p)
       for (int u = 0; u < kAUnroll; ++u) {
         const int64_t r = base + u * KPW + rg;
         const bool ok = r < r_hi;
-        kr[u] = ok ? R::load(kc + r * DH) : R::zero();
-        vr[u] = ok ? R::load(vc + r * DH) : R::zero();
+        kr[u] = ok ? (STREAM ? R::load_nt(kc + r * DH) : R::load(kc + r * DH)) : R::zero();
+        vr[u] = ok ? (STREAM ? R::load_nt(vc + r * DH) : R::load(vc + r * DH)) : R::zero();
       }
       float sc[kAUnroll];
       float vv[kAUnroll][8];
@@ -579,12 +581,23 @@ hipError_t launch_topk_attend(const TopkPlan& p, hipStream_t s) {
   const dim3 grid((unsigned)blocks), threads(kAW * 64);
   // candidate scores in dynamic LDS: at most max_pos / block of them
   const size_t lds = sizeof(float) * (size_t)(p.max_pos / p.block > 0 ? p.max_pos / p.block : 1);
+  const bool dec = p.pos != nullptr;
   if (p.bf16) {
-    if (p.Dh == 128) hipLaunchKernelGGL((topk_attend_kernel<bf16_t, 128>), grid, threads, lds, s, p);
-    else hipLaunchKernelGGL((topk_attend_kernel<bf16_t, 64>), grid, threads, lds, s, p);
+    if (p.Dh == 128) {
+      if (dec) hipLaunchKernelGGL((topk_attend_kernel<bf16_t, 128, true>), grid, threads, lds, s, p);
+      else hipLaunchKernelGGL((topk_attend_kernel<bf16_t, 128, false>), grid, threads, lds, s, p);
+    } else {
+      if (dec) hipLaunchKernelGGL((topk_attend_kernel<bf16_t, 64, true>), grid, threads, lds, s, p);
+      else hipLaunchKernelGGL((topk_attend_kernel<bf16_t, 64, false>), grid, threads, lds, s, p);
+    }
   } else {
-    if (p.Dh == 128) hipLaunchKernelGGL((topk_attend_kernel<float, 128>), grid, threads, lds, s, p);
-    else hipLaunchKernelGGL((topk_attend_kernel<float, 64>), grid, threads, lds, s, p);
+    if (p.Dh == 128) {
+      if (dec) hipLaunchKernelGGL((topk_attend_kernel<float, 128, true>), grid, threads, lds, s, p);
+      else hipLaunchKernelGGL((topk_attend_kernel<float, 128, false>), grid, threads, lds, s, p);
+    } else {
+      if (dec) hipLaunchKernelGGL((topk_attend_kernel<float, 64, true>), grid, threads, lds, s, p);
+      else hipLaunchKernelGGL((topk_attend_kernel<float, 64, false>), grid, threads, lds, s, p);
+    }
   }
   return hipGetLastError();
 }
