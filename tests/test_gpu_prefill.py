@@ -5,7 +5,7 @@ import torch
 
 import oracle
 from recurrence_augmented_dilated_amd import inputs
-from tests.gpu_util import BF16_TOL, F32_TOL, f64, need_gpu, report
+from tests.gpu_util import BF16_TOL, F32_TOL, RMS_TOL, f64, need_gpu, report
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -67,6 +67,22 @@ def test_segmented_scan_prefill(dtype, T):
     out = _gpu(x, dil, 0)
     err = report(f"segmented scan {dtype} T={T}", f64(out), _ref(x, dil, 0))
     assert err <= (F32_TOL if dtype == torch.float32 else BF16_TOL)
+
+
+@pytest.mark.parametrize("mu", [2.0, 9.0], ids=["mu2", "slow-decay"])
+def test_segmented_scan_multichunk_segments(mu):
+    """The segmented scan at 16 heads of 128 channels (32 slabs): on 256
+    compute units each slab gets 8 segments, so T = 6221 (25 chunks of 256
+    steps, the last one partial) gives segments of 4 chunks and a last segment
+    of one.  With mean logit 9 (g ~ 0.9999) the carry across every segment
+    boundary moves the grid states; D = 16 and 64 heads mixed."""
+    dil = [16, 64] * 8
+    x = inputs.prefill_inputs(1, 6221, 16, 128, dtype=torch.bfloat16, seed=77, mu=mu)
+    out = _gpu(x, dil, 0)
+    # rel_rms bound too: with mu = 9 the outputs are ~0.04, below any
+    # meaningful max-abs tolerance
+    err = report(f"segmented scan multi-chunk mu={mu}", f64(out), _ref(x, dil, 0), rms_max=RMS_TOL)
+    assert err <= BF16_TOL
 
 
 def test_per_head_dilation():
