@@ -668,6 +668,51 @@ def summarize_pmc(kernel, workload, fetch_dir, write_dir, cfetch_dir, cwrite_dir
     print(json.dumps(out))
 
 
+def summarize_counters(kernel, workload, dirs, bench_args):
+    """Every counter of one or more `rocprofv3 --pmc` runs (one counter set
+    per directory, the sets named in each run's own log), averaged per
+    dispatch of `kernel`, into profiles/<kernel>_<workload>_sq_counters.txt,
+    with the ratios read from them."""
+    import csv
+    pat = KERNEL_PATTERNS[kernel]
+    vals, cmds = {}, []
+    for d in dirs:
+        per = {}
+        with open(_find_csv(d, "counter_collection.csv")) as fh:
+            for r in csv.DictReader(fh):
+                if _matches(r["Kernel_Name"], pat):
+                    per.setdefault(r["Counter_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
+                    per[r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        for c, byd in per.items():
+            vals[c] = sum(byd.values()) / len(byd)
+        cmds.append(f"rocprofv3 --pmc {' '.join(sorted(per))} --output-format csv -d {d} -o pmc -- "
+                    f"python3 bench.py {bench_args}")
+    cmds.append(f"python3 bench.py --summarize-counters {kernel} {workload} {' '.join(dirs)} "
+                f"--pmc-bench-args '{bench_args}'")
+    lines = [f"SQ counters of {kernel} ({pat}) on workload {workload}, per dispatch", ""]
+    lines += ["$ " + c for c in cmds] + [""]
+    lines += [f"{c:28s} {v:.4g}" for c, v in sorted(vals.items())]
+    g = vals.get
+    derived = []
+    if g("SQ_WAVE_CYCLES"):
+        for c in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU"):
+            if g(c) is not None:
+                derived.append(f"{c} / SQ_WAVE_CYCLES = {g(c) / g('SQ_WAVE_CYCLES'):.3f}")
+    if g("SQ_VALU_MFMA_BUSY_CYCLES") and g("SQ_VALU_MFMA_COEXEC_CYCLES") is not None:
+        derived.append("SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES = "
+                       f"{g('SQ_VALU_MFMA_COEXEC_CYCLES') / g('SQ_VALU_MFMA_BUSY_CYCLES'):.3f}")
+    if g("SQ_INSTS_MFMA"):
+        for c in ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_VALU_TRANS_F32"):
+            if g(c) is not None:
+                derived.append(f"{c} / SQ_INSTS_MFMA = {g(c) / g('SQ_INSTS_MFMA'):.3f}")
+    if derived:
+        lines += ["", "derived:"] + derived
+    lines += ["", f"source sha256 of the kernel's files: {source_hash(kernel)}"]
+    with open(os.path.join(ROOT, "profiles", f"{kernel}_{workload}_sq_counters.txt"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_trace(trace_dir, kernel, workload, bench_args):
     """Launch statistics of `kernel` from a --kernel-trace --stats run into
     profiles/<kernel>_<workload>_kernel_trace.txt."""
@@ -717,6 +762,8 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=6, metavar=("KERNEL", "WORKLOAD", "FETCH_DIR", "WRITE_DIR",
                                                          "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="offline: write profiles/<KERNEL>_<WORKLOAD>_pmc.json from rocprofv3 counter CSVs")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="KERNEL WORKLOAD DIR",
+                    help="offline: average every counter of the given rocprofv3 --pmc runs per dispatch of KERNEL")
     ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_DIR", "KERNEL", "WORKLOAD"),
                     help="offline: write profiles/<KERNEL>_<WORKLOAD>_kernel_trace.txt from a "
                          "--kernel-trace --stats run")
@@ -727,6 +774,12 @@ def main():
         return
     if a.summarize_trace:
         summarize_trace(*a.summarize_trace, a.pmc_bench_args)
+        return
+    if a.summarize_counters:
+        if len(a.summarize_counters) < 3:
+            raise SystemExit("--summarize-counters KERNEL WORKLOAD DIR [DIR ...]")
+        k, w, *dirs = a.summarize_counters
+        summarize_counters(k, w, dirs, a.pmc_bench_args)
         return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
