@@ -60,6 +60,7 @@ def log(msg):
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "recurrence_augmented_dilated_amd", "csrc")
 KERNEL_SOURCES = {"scan": ["scan.hip", "rat_internal.h"], "attention": ["prefill_attn.hip", "rat_internal.h"],
+                  "attention_f32": ["prefill_attn.hip", "rat_internal.h"],
                   "decode": ["decode.hip", "kv_stream.h", "rat_internal.h"],
                   "topk_attend": ["topk.hip", "kv_stream.h", "rat_internal.h"],
                   "topk_stats": ["topk.hip", "rat_internal.h"], "topk_append": ["topk.hip", "rat_internal.h"],
@@ -598,6 +599,7 @@ def measure_copy(torch):
 # ---------------------------------------------------------------------------
 
 KERNEL_PATTERNS = {"scan": ("scan_kernel", "scan_seg_kernel"), "attention": "attn_bf16_kernel",
+                   "attention_f32": "attn_f32_kernel",
                    "decode": "decode_kernel",
                    "topk_attend": "topk_attend_kernel", "topk_stats": "topk_stats_kernel",
                    "topk_append": "topk_append_kernel", "grid_to_col": "grid_to_col_kernel",

@@ -37,6 +37,7 @@
 // staged in LDS) for fp32 inputs.
 #include <algorithm>
 
+#include "kv_stream.h"
 #include "rat_internal.h"
 
 namespace rat {
@@ -642,21 +643,24 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
 }
 
 // ---------------------------------------------------------------------------
-// fp32 kernel: exact fp32 arithmetic.  A block takes 64 queries; each query's
-// head dims are split over TPQ = DH / 8 lanes (8 dims per lane), so a block
-// has 8 (Dh = 64) or 16 (Dh = 128) waves and the per-key dot products are
-// short and independent (reduced over the TPQ lanes by shuffles)
+// fp32 kernel: exact fp32 arithmetic.  A block takes QB queries (64, or 16
+// when 64-query blocks would leave most compute units idle); each query's
+// head dims are split over TPQ = DH / 8 lanes (8 dims per lane), so the
+// per-key dot products are short and independent (reduced over the TPQ lanes
+// with DPP)
 // ---------------------------------------------------------------------------
 constexpr int kF32Keys = 32;
 constexpr int kF32Dims = 8;    // head dims per lane
 
-template <int DH>
-__global__ __launch_bounds__(64 * (DH / kF32Dims)) void attn_f32_kernel(const AttnArgs a) {
+template <int DH, int QB>
+__global__ __launch_bounds__(QB * (DH / kF32Dims)) void attn_f32_kernel(const AttnArgs a) {
   constexpr int TPQ = DH / kF32Dims;
-  constexpr int NT = 64 * TPQ;
+  constexpr int NT = QB * TPQ;
+  constexpr int LPT = kF32Keys * DH / (4 * NT);   // float4 loads of K (and of V) per lane and tile
+  static_assert(LPT >= 1 && LPT * 4 * NT == kF32Keys * DH, "whole float4 loads per tile");
   __shared__ __attribute__((aligned(16))) float sK[kF32Keys][DH];
   __shared__ __attribute__((aligned(16))) float sV[kF32Keys][DH];
-  __shared__ float sS[kF32Keys][64];   // each query's scores of the current tile
+  __shared__ float sS[kF32Keys][QB];   // each query's scores of the current tile
 
   int b, h, qtile;
   if (!attn_block(a, b, h, qtile)) return;
@@ -667,8 +671,8 @@ __global__ __launch_bounds__(64 * (DH / kF32Dims)) void attn_f32_kernel(const At
   const int D = a.heads.dil[h];
   const int64_t rowC = (int64_t)H * DH;
   const int P0 = a.p0;
-  const int t0 = qtile * 64;
-  const int t_last = min(t0 + 64, T) - 1;
+  const int t0 = qtile * QB;
+  const int t_last = min(t0 + QB, T) - 1;
   const int tq = t0 + qi;                 // query row; absolute position P0 + tq
   const bool q_live = tq < T;
   const int tqa = P0 + tq;
@@ -695,11 +699,12 @@ __global__ __launch_bounds__(64 * (DH / kF32Dims)) void attn_f32_kernel(const At
   const float* ak = W > 0 ? static_cast<const float*>(a.all_k) + (int64_t)b * a.arows * rowC + h * DH : nullptr;
   const float* av = W > 0 ? static_cast<const float*>(a.all_v) + (int64_t)b * a.arows * rowC + h * DH : nullptr;
 
-  // one float4 of K and one of V per lane and tile (row r, dims c..c+3); the
-  // next tile's are loaded while the current one is computed
-  static_assert(NT * 4 == kF32Keys * DH, "one float4 per lane and tile");
+  // LPT float4 of K and of V per lane and tile (rows r + u * NT * 4 / DH,
+  // dims c..c+3); the next tile's are loaded while the current one is
+  // computed
   const int r = tid * 4 / DH;
   const int c = tid * 4 - r * DH;
+  constexpr int RSTEP = NT * 4 / DH;   // rows between a lane's loads
   const int ntile = ntile_g + ntile_w;
   // first key row of tile `it`: grid row, or all-state buffer row (absolute
   // position - base) for a window tile; nvalid = rows of the tile in use
@@ -711,19 +716,23 @@ __global__ __launch_bounds__(64 * (DH / kF32Dims)) void attn_f32_kernel(const At
       nvalid = P0 + t_last + 1 - (row0 + a.base);
     }
   };
-  auto fetch = [&](int it, float4& kw, float4& vw) {
+  auto fetch = [&](int it, float4* kw, float4* vw) {
     int row0, nvalid;
     tile_rows(it, row0, nvalid);
-    kw = make_float4(0.f, 0.f, 0.f, 0.f);
-    vw = kw;
-    if (r < nvalid) {
-      const bool g = it < ntile_g;
-      const int64_t off = (int64_t)(row0 + r) * (g ? (int64_t)DH : rowC) + c;
-      kw = *reinterpret_cast<const float4*>((g ? gk : ak) + off);
-      vw = *reinterpret_cast<const float4*>((g ? gv : av) + off);
+    const bool g = it < ntile_g;
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int rr = r + u * RSTEP;
+      kw[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      vw[u] = kw[u];
+      if (rr < nvalid) {
+        const int64_t off = (int64_t)(row0 + rr) * (g ? (int64_t)DH : rowC) + c;
+        kw[u] = *reinterpret_cast<const float4*>((g ? gk : ak) + off);
+        vw[u] = *reinterpret_cast<const float4*>((g ? gv : av) + off);
+      }
     }
   };
-  float4 kw, vw;
+  float4 kw[LPT], vw[LPT];
   if (ntile > 0) fetch(0, kw, vw);
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -732,8 +741,11 @@ __global__ __launch_bounds__(64 * (DH / kF32Dims)) void attn_f32_kernel(const At
     int row0, nvalid;
     tile_rows(it, row0, nvalid);
     __syncthreads();
-    *reinterpret_cast<float4*>(&sK[r][c]) = kw;
-    *reinterpret_cast<float4*>(&sV[r][c]) = vw;
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      *reinterpret_cast<float4*>(&sK[r + u * RSTEP][c]) = kw[u];
+      *reinterpret_cast<float4*>(&sV[r + u * RSTEP][c]) = vw[u];
+    }
     __syncthreads();
     if (it + 1 < ntile) fetch(it + 1, kw, vw);
     // the tile's scores first (masked keys -inf), then one rescale of the
@@ -751,8 +763,7 @@ __global__ __launch_bounds__(64 * (DH / kF32Dims)) void attn_f32_kernel(const At
       float sp = 0.f;
 #pragma unroll
       for (int i = 0; i < kF32Dims; ++i) sp = fmaf(q[i], sK[kk][d0 + i], sp);
-#pragma unroll
-      for (int o = 1; o < TPQ; o <<= 1) sp += __shfl_xor(sp, o);
+      sp = group_sum<TPQ>(sp);   // DPP within the query's TPQ adjacent lanes
       const float sc = valid ? sp * a.sl2 : -INFINITY;   // uniform across the lanes of one query
       sS[kk][qi] = sc;   // every lane of a query stores the same value
       tmax = fmaxf(tmax, sc);
@@ -845,12 +856,24 @@ hipError_t launch_prefill_attention(const AttnPlan& p, hipStream_t s) {
       hipLaunchKernelGGL((attn_bf16_kernel<64, false>), dim3(blocks), dim3(kWaves * 64), 0, s, a);
     }
   } else {
-    a.n_qtiles = (p.T + 63) / 64;
+    // 64-query blocks unless that leaves fewer blocks than compute units
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorInvalidDevice;
+    const bool small = (int64_t)p.B * p.H * ((p.T + 63) / 64) < cus;
+    a.n_qtiles = small ? (p.T + 15) / 16 : (p.T + 63) / 64;
     const int blocks = set_classes(p, a);
-    if (p.Dh == 128)
-      hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(blocks), dim3(64 * (128 / kF32Dims)), 0, s, a);
-    else
-      hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(blocks), dim3(64 * (64 / kF32Dims)), 0, s, a);
+    if (small) {
+      if (p.Dh == 128)
+        hipLaunchKernelGGL((attn_f32_kernel<128, 16>), dim3(blocks), dim3(16 * (128 / kF32Dims)), 0, s, a);
+      else
+        hipLaunchKernelGGL((attn_f32_kernel<64, 16>), dim3(blocks), dim3(16 * (64 / kF32Dims)), 0, s, a);
+    } else if (p.Dh == 128) {
+      hipLaunchKernelGGL((attn_f32_kernel<128, 64>), dim3(blocks), dim3(64 * (128 / kF32Dims)), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((attn_f32_kernel<64, 64>), dim3(blocks), dim3(64 * (64 / kF32Dims)), 0, s, a);
+    }
   }
   return hipGetLastError();
 }
