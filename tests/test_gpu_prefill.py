@@ -49,6 +49,17 @@ def test_fp32_small(D, W):
     assert err <= F32_TOL
 
 
+@pytest.mark.parametrize("Dh", [64, 128])
+def test_fp32_64query_blocks(Dh):
+    """fp32 with at least as many 64-query blocks as compute units (2 x 8
+    heads x 18 q-tiles = 288), so the exact-fp32 kernel runs with 64-query
+    blocks (smaller launches use 16-query blocks); ragged T, a window."""
+    x = inputs.prefill_inputs(2, 1100, 8, Dh, dtype=torch.float32, seed=40 + Dh)
+    out = _gpu(x, 4, 16)
+    err = report(f"fp32 64-query blocks Dh={Dh}", f64(out), _ref(x, 4, 16))
+    assert err <= F32_TOL
+
+
 def test_bf16_dh64_batch():
     x = inputs.prefill_inputs(3, 257, 4, 64, dtype=torch.bfloat16, seed=11)
     out = _gpu(x, 4, 16)
