@@ -646,8 +646,7 @@ __global__ __launch_bounds__(kSegNW * 64) void scan_seg_kernel(const ScanArgs a)
                                       : grow0 + i * a.Dh + d;
   };
   // the same entry's (A, B) pair in part[]: head-major in both layouts, so
-  // that a block's pairs fill one run of memory in entry order (pairs
-  // scattered over the token-major rows slow the input stream down)
+  // that a block's pairs fill one run of memory in entry order
   auto part_elem = [&](int64_t i) __attribute__((always_inline)) -> int64_t {
     return tn.grid_mode == kGridToken ? (((int64_t)b * a.H + h) * G_tok + i) * a.Dh + d
                                       : grow0 + i * a.Dh + d;
@@ -678,9 +677,9 @@ __global__ __launch_bounds__(kSegNW * 64) void scan_seg_kernel(const ScanArgs a)
   typename V::raw xr[kLW];
   typename Z::raw zr[kLW];
   // step s of this wave's kLW steps from row t0.  Rows past T read row T-1
-  // (pass 1 leaves such steps out): no branch around the loads, so the
-  // compiler's wait counts stay exact and the loads of the next chunk stay
-  // in flight under the current one.
+  // (what phase A folds in from them reaches no stored value): no branch
+  // around the loads, so the compiler's wait counts stay exact and the loads
+  // of the next chunk stay in flight under the current one.
   // The inputs are read once, as a stream: non-temporal loads, which keep
   // them from displacing the (A, B) pairs from the caches on their way to
   // memory (with plain loads the scan runs ~9% slower on T = 262144).
