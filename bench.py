@@ -764,8 +764,10 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=6, metavar=("KERNEL", "WORKLOAD", "FETCH_DIR", "WRITE_DIR",
                                                          "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="offline: write profiles/<KERNEL>_<WORKLOAD>_pmc.json from rocprofv3 counter CSVs")
-    ap.add_argument("--summarize-counters", nargs="+", metavar="KERNEL WORKLOAD DIR",
-                    help="offline: average every counter of the given rocprofv3 --pmc runs per dispatch of KERNEL")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="ARG",
+                    help="offline: KERNEL WORKLOAD DIR [DIR ...]: average every counter of the given "
+                         "rocprofv3 --pmc runs per dispatch of KERNEL into "
+                         "profiles/<KERNEL>_<WORKLOAD>_sq_counters.txt")
     ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_DIR", "KERNEL", "WORKLOAD"),
                     help="offline: write profiles/<KERNEL>_<WORKLOAD>_kernel_trace.txt from a "
                          "--kernel-trace --stats run")
