@@ -11,11 +11,11 @@
 // channels and kLW time steps; a block of kNW waves covers kNW*kLW steps (a
 // "chunk") of one channel slab.  Every input element is read from HBM once
 // and kept in registers as loaded (bf16/fp32 x, fp32 z): a first pass turns
-// every z into 1 - g in place and folds the wave's steps into an aggregate
-// (A = prod g, B = state reached from a zero carry), and once the chunk's
-// carry-in is known a second pass re-runs the recurrence from it over the
-// same registers (g = 1 - (1 - g): one subtraction per element, no second
-// sigmoid) and stores the states.
+// every z into c = 1 - g in place and folds the wave's steps into an
+// aggregate (A = prod g, B = state reached from a zero carry), and once the
+// chunk's carry-in is known a second pass re-runs the recurrence from it over
+// the same registers (h - c h + c x: two FMAs per element, no second sigmoid
+// and no rounded 1 - c) and stores the states.
 //
 // Carry propagation across chunks is a decoupled look-back.  Block b of the
 // grid handles chunk b / n_slabs of slab b % n_slabs, publishes its chunk
@@ -174,12 +174,11 @@ __device__ void chunk_aggregate(const XT* x, const float* z, int64_t C, int T, i
   const int t_end = min(T, (j + 1) * kChunkT);
   for (int t = j * kChunkT; t < t_end; ++t) {
     const float c = gate_comp(z[(int64_t)t * C]);
-    float g = 1.f - c;
-    if (RESET && (p0 + t) % reset == 0) g = 0.f;   // restart: the carried state is dropped
+    const bool restart = RESET && (p0 + t) % reset == 0;   // the carried state is dropped
     const float xv = sizeof(XT) == 2 ? bf16_to_f32(reinterpret_cast<const bf16_t*>(x)[(int64_t)t * C])
                                      : reinterpret_cast<const float*>(x)[(int64_t)t * C];
-    Bv = g * Bv + c * xv;
-    A *= g;
+    Bv = restart ? c * xv : fmaf(c, xv, fmaf(-c, Bv, Bv));   // (1 - c) B + c x
+    A = restart ? 0.f : fmaf(-A, c, A);
   }
 }
 
@@ -344,13 +343,13 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
       if (rs) next_reset = sat_add(next_reset, a.reset_every);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        float cc = gate_comp(Z::get(zr[s], c));
+        const float cc = gate_comp(Z::get(zr[s], c));
         Z::set(zr[s], c, cc);   // pass 2 reads 1 - g from here
-        float g = 1.f - cc;
-        if (rs) g = 0.f;
-        if (!live) { g = 1.f; cc = 0.f; }
-        hl[c] = g * hl[c] + cc * V::get(xr[s], c);
-        pp[c] *= g;
+        const float xv = V::get(xr[s], c);
+        const float hn = rs ? cc * xv : fmaf(cc, xv, fmaf(-cc, hl[c], hl[c]));   // (1 - c) h + c x
+        const float pn = rs ? 0.f : fmaf(-pp[c], cc, pp[c]);                     // (1 - c) p
+        hl[c] = live ? hn : hl[c];   // a step past T (a repeated row) leaves the aggregate alone
+        pp[c] = live ? pn : pp[c];
       }
     }
 #pragma unroll
@@ -444,9 +443,9 @@ __global__ __launch_bounds__(kNW * 64) void scan_kernel(const ScanArgs a) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const float cc = Z::get(zr[s], c);
-        float g = 1.f - cc;
-        if (rs) g = 0.f;   // chunk start: the state restarts from zero
-        hv[c] = g * hv[c] + cc * V::get(xr[s], c);
+        const float xv = V::get(xr[s], c);
+        // (1 - c) h + c x; at a chunk start the state restarts from zero
+        hv[c] = rs ? cc * xv : fmaf(cc, xv, fmaf(-cc, hv[c], hv[c]));
       }
       if (tok_all) V::store(out_all + ((int64_t)b * a.arows + a.all_row0 + t) * C + cs * SC + lo, hv);
       if (out_grid && t == next_grid) {
