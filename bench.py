@@ -868,7 +868,8 @@ def prefill_result(cfg_id, c, a, torch, R, inputs, cpu):
                  "traffic": measured_traffic("scan", wkey)},
         "attention": {"bound": "mfma" if bf16 else "alu", "ms": p["ms_attn"], "achieved": attn_tfs / 1e12,
                       "peak": attn_peak / 1e12, "unit": "TFLOP/s", "frac": attn_tfs / attn_peak,
-                      "algorithmic_flops": w["attn_flops"], "traffic": measured_traffic("attention", wkey)},
+                      "algorithmic_flops": w["attn_flops"],
+                      "traffic": measured_traffic("attention" if bf16 else "attention_f32", wkey)},
     }
     dom = "scan" if p["ms_scan"] >= p["ms_attn"] else "attention"
     k = kernels[dom]
