@@ -102,13 +102,12 @@ __device__ __forceinline__ void block_coords(int bid, int B, int H, int n_qtiles
   h = p - b * H;
 }
 
-// Block -> (b, h, q-tile) over the dilation classes: a class's blocks run
+// Work item -> (b, h, q-tile) over the dilation classes: a class's blocks run
 // before those of sparser heads, so the heads whose key sets outgrow an XCD's
 // L2 have their q-tiles in flight together and stream the same keys; within a
 // class block_coords applies.  Every class but the last is padded to a
 // multiple of 8 blocks, which keeps its XCD pinning; padding blocks get false.
-__device__ __forceinline__ bool attn_block(const AttnArgs& a, int& b, int& h, int& qtile) {
-  const int bid = blockIdx.x;
+__device__ __forceinline__ bool attn_block(const AttnArgs& a, int bid, int& b, int& h, int& qtile) {
   int c = 0;
   while (c + 1 < a.ncls && bid >= a.cls_b0[c + 1]) ++c;
   const int nh = a.cls_h0[c + 1] - a.cls_h0[c];
@@ -176,11 +175,29 @@ __device__ __forceinline__ void load_lds16(const void* base, uint32_t voff, void
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory");
 }
 
-// Wait until at most n of this wave's vector-memory operations are pending.
+// Wait until at most N of this wave's vector-memory operations are pending
+// (vmcnt is six bits: the low four in bits 3:0, the high two in bits 15:14).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8));
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// The same for a run-time, wave-uniform bound n: waits for the largest
+// multiple of G (at most 8 G) that does not exceed n, which is at least as
+// long as a wait for n itself.
+template <int G>
+__device__ __forceinline__ void wait_vmcnt_atmost(int n) {
+  if (n == G) wait_vmcnt<G>();
+  else if (n >= 8 * G) wait_vmcnt<8 * G>();
+  else if (n >= 7 * G) wait_vmcnt<7 * G>();
+  else if (n >= 6 * G) wait_vmcnt<6 * G>();
+  else if (n >= 5 * G) wait_vmcnt<5 * G>();
+  else if (n >= 4 * G) wait_vmcnt<4 * G>();
+  else if (n >= 3 * G) wait_vmcnt<3 * G>();
+  else if (n >= 2 * G) wait_vmcnt<2 * G>();
+  else if (n >= G) wait_vmcnt<G>();
+  else wait_vmcnt<0>();
 }
 
 // Ring barrier: this wave's LDS reads are complete, then all waves meet.  A
@@ -216,7 +233,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
   __shared__ __attribute__((aligned(1024))) char sV[4][VBYTES];
 
   int b, h, qtile;
-  if (!attn_block(a, b, h, qtile)) return;
+  if (!attn_block(a, blockIdx.x, b, h, qtile)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -643,6 +660,485 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
 }
 
 // ---------------------------------------------------------------------------
+// bf16 MFMA kernel, persistent form for grid-only key sets (W = 0)
+// ---------------------------------------------------------------------------
+//
+// One block per compute unit walks a list of q-tiles (the work items of the
+// one-block-per-q-tile launch) and streams their 64-key tiles through one
+// three-slot ring as if they were one sequence: the next q-tile's Q rows and
+// first tiles load while the current q-tile's last tiles are computed, so no
+// block start, Q landing or first-tile wait sits between q-tiles.  The tile
+// math is that of attn_bf16_kernel.  Each wave owns a staging area for its
+// 32 query rows: the next q-tile's Q rows land there by direct loads while
+// the current q-tile runs and are read into fragments once its last tile's
+// scores are taken (the old fragments are dead then); the current q-tile's
+// output rows are staged there after that and stored as whole rows.  The Q
+// rows of the q-tile after the next wait until the area is free again, so
+// the loads run at most one q-tile ahead.
+//
+// Item order: within an XCD (blocks and items are dealt to the XCDs by index
+// mod 8, which keeps every (b, h) pair on one XCD as in the plain launch) the
+// heaviest-first item list is cut into rounds of one item per block, dealt
+// ascending in even rounds and descending in odd ones, which evens out the
+// per-block sums of a list whose costs fall steadily.
+//
+// Waits: this wave's loads complete in issue order, so a tile has landed once
+// at most as many vector-memory operations are pending as loads were issued
+// after it.  Stores are never counted: a pending store only makes such a wait
+// longer, whatever the order in which stores complete.
+constexpr int kPSlots = 3;   // one tile consumed, two in flight
+
+struct StreamItem {
+  int b, h, t0, ntiles;
+};
+struct StreamSrc {   // where an item's tiles come from
+  const char* gk;    // grid keys of (b, h), row-major
+  const char* gvt;   // grid values of (b, h), transposed
+  int ng_hi, cap;
+};
+
+// A copy of x that the compiler must treat as new: values derived from it
+// are recomputed where they are used instead of being hoisted out of the
+// loop and kept live (or spilled) across it.
+__device__ __forceinline__ uint32_t opaque_s(uint32_t x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+__device__ __forceinline__ uint32_t opaque_v(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void_t*)p));
+}
+// load_lds16 with the LDS address given as a number
+__device__ __forceinline__ void load_lds16_to(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory");
+}
+
+template <int DH>
+__global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_stream_kernel(const AttnArgs a) {
+  constexpr int KS = DH / 16;
+  constexpr int DB = DH / 32;
+  constexpr int KROW = DH * 2;
+  constexpr int LPR = KROW / 16;
+  constexpr int KBYTES = kBN * KROW;
+  constexpr int VBYTES = DH * kBN * 2;
+  constexpr int KL = KBYTES / 1024 / kWaves;
+  constexpr int VL = VBYTES / 1024 / kWaves;
+  constexpr int LPW = KL + VL;       // direct loads per wave per tile
+  constexpr int CPR = DH / 8;        // 16-byte chunks per query / output row
+  constexpr int RPI = 64 / CPR;      // rows per load / store instruction
+  constexpr int QL = 32 / RPI;       // instructions for a wave's 32 rows
+  constexpr int AREA = 32 * KROW;    // a wave's staging area
+  static_assert(KL >= 1 && VL >= 1 && KL * kWaves * 1024 == KBYTES && VL * kWaves * 1024 == VBYTES, "tiles");
+  static_assert(QL * 1024 == AREA, "staging area");
+  constexpr int G = QL < LPW ? QL : LPW;   // every load count is a multiple of G
+  static_assert(QL % G == 0 && LPW % G == 0, "load counts");
+
+  __shared__ __attribute__((aligned(1024))) char sK[kPSlots][KBYTES];
+  __shared__ __attribute__((aligned(1024))) char sV[kPSlots][VBYTES];
+  __shared__ __attribute__((aligned(1024))) char sA[kWaves][AREA];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31;
+  const int g = lane >> 5;
+  const int T = a.T;
+  const int64_t rowC = (int64_t)a.H * DH;
+  const int P0 = a.p0;
+  char* const wa = sA[wave];
+
+  // ---- the block's items
+  const int nb = a.cls_b0[a.ncls];
+  const int xcd = blockIdx.x & 7;
+  const int li = blockIdx.x >> 3;
+  const int nbx = gridDim.x >> 3;                  // blocks per XCD
+  const int nrounds = ((nb + 7) / 8 + nbx - 1) / nbx;
+  auto item_at = [&](int r, StreamItem& it) __attribute__((always_inline)) -> bool {
+    const int k = r * nbx + ((r & 1) ? nbx - 1 - li : li);
+    const int bid = 8 * k + xcd;
+    int qtile;
+    if (bid >= nb || !attn_block(a, bid, it.b, it.h, qtile)) return false;
+    it.t0 = qtile * kBM;
+    it.ntiles = ((P0 + min(it.t0 + kBM, T)) / a.heads.dil[it.h] + kBN - 1) / kBN;
+    return true;
+  };
+  auto src_of = [&](const StreamItem& it) __attribute__((always_inline)) -> StreamSrc {
+    StreamSrc r;
+    r.ng_hi = (P0 + min(it.t0 + kBM, T)) / a.heads.dil[it.h];   // grid entries of the last row
+    r.cap = a.vgcap[it.h];
+    r.gk = reinterpret_cast<const char*>(static_cast<const bf16_t*>(a.grid_k) +
+                                         grid_row_offset(a.heads, a.B, it.b, it.h, 0, DH));
+    r.gvt = reinterpret_cast<const char*>(static_cast<const bf16_t*>(a.grid_v) +
+                                          ((int64_t)a.B * a.vgoff[it.h] + (int64_t)it.b * r.cap) * DH);
+    return r;
+  };
+  // rows t0 + wave * 32 + r (r < 32) of head h; rows past T are not written
+  auto out_rows = [&](const StreamItem& it) __attribute__((always_inline)) {
+    return static_cast<bf16_t*>(a.out) + ((int64_t)it.b * T + it.t0 + wave * 32) * rowC + it.h * DH;
+  };
+  // next item with keys after round r (r advances to it); items without keys
+  // on the way get their zero rows
+  auto advance = [&](int& r, StreamItem& it) __attribute__((always_inline)) -> bool {
+    while (++r < nrounds) {
+      if (!item_at(r, it)) continue;
+      if (it.ntiles > 0) return true;
+      bf16_t* ob = out_rows(it);
+      const uint32_t l = opaque_v(uint32_t(lane));
+#pragma unroll
+      for (int i = 0; i < QL; ++i) {
+        const uint32_t rr = i * RPI + l / CPR;
+        if (it.t0 + wave * 32 + int(rr) < T)
+          *reinterpret_cast<uint4*>(ob + __umul24(rr, uint32_t(rowC)) + 8 * (l % CPR)) = make_uint4(0, 0, 0, 0);
+      }
+    }
+    return false;
+  };
+
+  // ---- direct loads
+  // Q rows of the wave into its area: row r, physical chunk p holds logical
+  // chunk p ^ (r mod CPR); rows past T re-read row T - 1
+  auto issue_q = [&](const StreamItem& it) __attribute__((always_inline)) {
+    const int r0 = min(it.t0 + wave * 32, T - 1);
+    const uint32_t rmax = uint32_t(T - 1 - r0);
+    const char* base = reinterpret_cast<const char*>(static_cast<const bf16_t*>(a.q) +
+                                                     ((int64_t)it.b * T + r0) * rowC + it.h * DH);
+    const uint32_t l = opaque_v(uint32_t(lane));
+    const uint32_t q = l / CPR;                      // row within the instruction's RPI rows
+    const uint32_t c0 = 16u * ((l % CPR) ^ q);       // its chunk, before the row's swizzle bits
+    const uint32_t wb = opaque_s(lds_addr(wa));
+#pragma unroll
+    for (int i = 0; i < QL; ++i) {
+      // row i * RPI + q: (i * RPI) mod CPR is a multiple of RPI > q, so the
+      // row's swizzle is c0 ^ that
+      const uint32_t r = min(uint32_t(i * RPI) + q, rmax);
+      const uint32_t off = __umul24(r, uint32_t(rowC * 2)) + (c0 ^ (16u * uint32_t((i * RPI) & (CPR - 1))));
+      load_lds16_to(base, off, wb + i * 1024);
+    }
+  };
+  int k_row[KL];
+  uint32_t k_chunk[KL], v_row2[VL];
+#pragma unroll
+  for (int u = 0; u < KL; ++u) {
+    const int j = wave * KL + u;
+    const int r = j * (64 / LPR) + lane / LPR;
+    const int p = lane % LPR;
+    k_row[u] = r;
+    k_chunk[u] = 16u * uint32_t(p ^ (r & (LPR - 1) & 15));
+  }
+#pragma unroll
+  for (int u = 0; u < VL; ++u) v_row2[u] = 2u * uint32_t((wave * VL + u) * 8 + lane / 8);
+  const uint32_t v_col = 16u * uint32_t(lane % 8);
+  // tile t of the item whose source is src, into ring slot S
+  auto issue_tile = [&](const StreamSrc& src, int t, auto Sc) __attribute__((always_inline)) {
+    constexpr int S = decltype(Sc)::value;
+    const int row0 = t * kBN;
+    const int nvalid = src.ng_hi - row0;
+    const char* kb = src.gk + (int64_t)row0 * KROW;
+    const char* vb = src.gvt + (int64_t)row0 * 2;
+    const uint32_t kd = opaque_s(lds_addr(sK[0]) + uint32_t(wave * KL * 1024));
+    const uint32_t vd = opaque_s(lds_addr(sV[0]) + uint32_t(wave * VL * 1024));
+#pragma unroll
+    for (int u = 0; u < KL; ++u)
+      load_lds16_to(kb, uint32_t(min(k_row[u], nvalid - 1)) * KROW + k_chunk[u], kd + S * KBYTES + u * 1024);
+#pragma unroll
+    for (int u = 0; u < VL; ++u)
+      load_lds16_to(vb, v_row2[u] * uint32_t(src.cap) + v_col, vd + S * VBYTES + u * 1024);
+  };
+
+  uint32_t vo[4][2];
+#pragma unroll
+  for (int st = 0; st < 4; ++st)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int d = 32 * p + n;
+      vo[st][p] = uint32_t(d * (kBN * 2) + 16 * ((2 * st + g) ^ col_swz(d)));
+    }
+  auto v_at = [&](const char* cV, int st, int db) __attribute__((always_inline)) -> uint4 {
+    return *reinterpret_cast<const uint4*>(cV + vo[st][db & 1] + (db >> 1) * (64 * kBN * 2));
+  };
+
+  // ---- consumer state of the current item
+  bf16x8_t qf[KS];
+  floatx16_t o[DB];
+  float m_run, l_run;
+  int ng_me, ng_w0, ng_w1;
+  bool wave_live;
+  auto enter = [&](const StreamItem& it) __attribute__((always_inline)) {
+    const int D = a.heads.dil[it.h];
+    const int tq = it.t0 + wave * 32 + n;
+    ng_me = tq < T ? (P0 + tq + 1) / D : 0;
+    wave_live = it.t0 + wave * 32 < T;
+    ng_w0 = wave_live ? (P0 + it.t0 + wave * 32 + 1) / D : 0;
+    ng_w1 = wave_live ? (P0 + min(it.t0 + wave * 32 + 31, T - 1) + 1) / D : 0;
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
+    m_run = -INFINITY;
+    l_run = 0.f;
+  };
+  auto read_q = [&]() __attribute__((always_inline)) {
+    const uint32_t l = opaque_v(uint32_t(lane));
+    const uint32_t ln = l & 31, lg = l >> 5;
+    const char* row = wa + ln * KROW;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
+                                                row + (((2 * ks + lg) ^ (ln & (CPR - 1))) << 4)));
+  };
+
+  auto scores = [&](const char* cK, floatx16_t* sc) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int m = 32 * kb + n;
+        const int c = (2 * ks + g) ^ (m & (LPR - 1) & 15);
+        const uint4 w = *reinterpret_cast<const uint4*>(cK + m * KROW + 16 * c);
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), qf[ks], sc[kb], 0, 0, 0);
+      }
+    constexpr int NM = 2 * KS, LEAD = 6;
+#pragma unroll
+    for (int i = 0; i < LEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + LEAD < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+
+  auto finish = [&](int kbase, bool masked, const char* cV, floatx16_t* s) __attribute__((always_inline)) {
+    if (masked) {
+      // grid key kbase + 4g + c is valid iff c <= ng_me - 1 - kbase - 4g
+      const int key0 = kbase + 4 * g;
+      const int lo = -64;
+      const int hi = ng_me - 1 - key0;
+      const bool none = hi < lo;
+      const int lo2 = none ? 1 << 20 : lo;
+      const uint32_t span = none ? 0u : uint32_t(hi - lo);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
+          s[kb][r] = uint32_t(c - lo2) <= span ? s[kb][r] : -INFINITY;
+        }
+    }
+    uint4 vpre[2 * DB];
+#pragma unroll
+    for (int j = 0; j < 2 * DB; ++j) vpre[j] = v_at(cV, j / DB, j % DB);
+
+    float mx_lo, mx_hi;
+    half_pair(tree_max32(s), mx_lo, mx_hi);
+    const float mt = __builtin_elementwise_maximum(mx_lo, mx_hi) * a.sl2;
+    const bool up = mt > m_run + kLazy;
+    if (__ballot(up) != 0) {
+      const float m_new = up ? mt : m_run;
+      const float alpha = up ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+      m_run = m_new;
+    }
+    const float nm = m_run == -INFINITY ? 0.f : -m_run;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], a.sl2, nm));
+
+    uint4 pws[4];
+    float lp0 = 0.f, lp1 = 0.f;
+    const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int kb = st >> 1;
+      const int r0 = 8 * (st & 1);
+      pws[st].x = pack_bf16x2(s[kb][r0 + 0], s[kb][r0 + 1]);
+      pws[st].y = pack_bf16x2(s[kb][r0 + 2], s[kb][r0 + 3]);
+      pws[st].z = pack_bf16x2(s[kb][r0 + 4], s[kb][r0 + 5]);
+      pws[st].w = pack_bf16x2(s[kb][r0 + 6], s[kb][r0 + 7]);
+      lp0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pws[st].x), ones, lp0, false);
+      lp1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pws[st].y), ones, lp1, false);
+      lp0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pws[st].z), ones, lp0, false);
+      lp1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pws[st].w), ones, lp1, false);
+    }
+    l_run += lp0 + lp1;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pws[st]);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const uint4 vw = st < 2 ? vpre[st * DB + db] : v_at(cV, st, db);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vw), pf, o[db], 0, 0, 0);
+      }
+    }
+  };
+
+  // normalised output rows of the current item into the wave's area
+  // (row-major, chunks XOR-swizzled by row)
+  auto stage = [&]() __attribute__((always_inline)) {
+    float l_lo, l_hi;
+    half_pair(l_run, l_lo, l_hi);
+    const float l_tot = l_lo + l_hi;
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    const uint32_t l = opaque_v(uint32_t(lane));
+    const uint32_t ln = l & 31, lg = l >> 5;
+    char* const row = wa + ln * KROW + 8 * lg;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const uint32_t c = 4 * db + k4;
+        const uint2 w = make_uint2(pack_bf16x2(o[db][4 * k4 + 0] * inv, o[db][4 * k4 + 1] * inv),
+                                   pack_bf16x2(o[db][4 * k4 + 2] * inv, o[db][4 * k4 + 3] * inv));
+        *reinterpret_cast<uint2*>(row + ((c ^ (ln & (CPR - 1))) << 4)) = w;
+      }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the rows are in LDS
+    asm volatile("" ::: "memory");
+  };
+  // the staged rows of item `it` out as whole rows; afterwards the area is free
+  auto flush = [&](const StreamItem& it) __attribute__((always_inline)) {
+    bf16_t* ob = out_rows(it);
+    const uint32_t l2 = opaque_v(uint32_t(lane));
+    const uint32_t q = l2 / CPR, p = l2 % CPR;
+#pragma unroll
+    for (int i = 0; i < QL; ++i) {
+      const uint32_t r = i * RPI + q;
+      const uint4 w = *reinterpret_cast<const uint4*>(wa + r * KROW + (p << 4));
+      if (it.t0 + wave * 32 + int(r) < T)
+        *reinterpret_cast<uint4*>(ob + __umul24(r, uint32_t(rowC)) + ((p ^ (r & (CPR - 1))) << 3)) = w;
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // the area is read before it takes new Q rows
+    asm volatile("" ::: "memory");
+  };
+
+  // ---- prologue: the first item's Q rows and up to two of its tiles
+  StreamItem C, N;
+  int rN = -1;
+  if (!advance(rN, C)) return;
+  bool hasN = advance(rN, N);
+  enter(C);
+  int loads = 0;              // direct loads this wave has issued (stores are not counted)
+  int e[kPSlots] = {0, 0, 0};  // value of `loads` right after the tile in each slot was issued
+  issue_q(C);
+  loads += QL;
+  StreamSrc I = src_of(C);    // the issue cursor's item (C, or N once C's tiles are out)
+  int I_ntiles = C.ntiles;
+  issue_tile(I, 0, std::integral_constant<int, 0>{});
+  loads += LPW;
+  e[0] = loads;
+  int iss = 1;                // its next tile
+  bool curN = false;          // the issue cursor is in N
+  int qN = 0;                 // value of `loads` right after N's Q rows were issued
+  int ahead = 0;              // tiles issued beyond the one being consumed
+  if (C.ntiles > 1) {
+    issue_tile(I, 1, std::integral_constant<int, 1>{});
+    loads += LPW;
+    e[1] = loads;
+    iss = 2;
+    ahead = 1;
+  }
+  wait_vmcnt_atmost<G>(loads - e[0]);   // Q rows and tile 0 have landed
+  read_q();
+  ring_barrier();
+
+  // issue the next tile of the stream into slot S, if it exists and its
+  // item is C or N; entering N first sends N's Q rows into the area (free
+  // since C's Q rows were read and the previous output rows went out)
+  auto issue_next = [&](auto Sc) __attribute__((always_inline)) -> bool {
+    if (iss == I_ntiles) {
+      if (curN || !hasN) return false;
+      curN = true;
+      I = src_of(N);
+      I_ntiles = N.ntiles;
+      iss = 0;
+      issue_q(N);
+      loads += QL;
+      qN = loads;
+    }
+    constexpr int S = decltype(Sc)::value;
+    issue_tile(I, iss++, Sc);
+    loads += LPW;
+    e[S] = loads;
+    return true;
+  };
+
+  floatx16_t sc[2];
+  int jt = 0;                 // tile of C in the slot being consumed
+  bool done = false;
+  // the previous item's output rows wait in the area until the next step
+  // begins, so that their stores complete under that step's work instead of
+  // lengthening the wait that ends this one
+  StreamItem P = C;
+  bool pend = false;
+  auto step = [&](auto Sc) __attribute__((always_inline)) {
+    constexpr int S = decltype(Sc)::value;
+    constexpr int S1 = (S + 1) % kPSlots, S2 = (S + 2) % kPSlots;
+    const int kbase = jt * kBN;
+    const bool needed = wave_live && kbase < ng_w1;
+    const bool masked = kbase + kBN > ng_w0;
+    if (pend) {
+      flush(P);
+      pend = false;
+    }
+    // tiles jt + 1 and jt + 2 of the stream go into the other two slots
+    if (ahead == 0 && issue_next(std::integral_constant<int, S1>{})) ahead = 1;
+    if (ahead == 1 && issue_next(std::integral_constant<int, S2>{})) ahead = 2;
+    if (needed) scores(sK[S], sc);
+    if (needed) finish(kbase, masked, sV[S], sc);
+    if (++jt == C.ntiles) {
+      // item end: N's Q fragments (the old ones are dead), then C's output
+      if (hasN) {
+        wait_vmcnt_atmost<G>(loads - qN);
+        read_q();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the fragments are read
+        asm volatile("" ::: "memory");
+      }
+      stage();
+      if (!hasN) {
+        flush(C);
+        done = true;
+        return;
+      }
+      P = C;
+      pend = true;
+      C = N;
+      curN = false;
+      enter(C);
+      jt = 0;
+      hasN = advance(rN, N);
+    }
+    // the next tile has landed (this wave's part of it), then all waves meet
+    wait_vmcnt_atmost<G>(loads - e[S1]);
+    ring_barrier();
+    --ahead;
+  };
+  using Slot0 = std::integral_constant<int, 0>;
+  using Slot1 = std::integral_constant<int, 1>;
+  using Slot2 = std::integral_constant<int, 2>;
+  for (;;) {
+    step(Slot0{});
+    if (done) break;
+    step(Slot1{});
+    if (done) break;
+    step(Slot2{});
+    if (done) break;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 kernel: exact fp32 arithmetic.  A block takes QB queries (64, or 16
 // when 64-query blocks would leave most compute units idle); each query's
 // head dims are split over TPQ = DH / 8 lanes (8 dims per lane), so the
@@ -663,7 +1159,7 @@ __global__ __launch_bounds__(QB * (DH / kF32Dims)) void attn_f32_kernel(const At
   __shared__ float sS[kF32Keys][QB];   // each query's scores of the current tile
 
   int b, h, qtile;
-  if (!attn_block(a, b, h, qtile)) return;
+  if (!attn_block(a, blockIdx.x, b, h, qtile)) return;
   const int tid = threadIdx.x;
   const int qi = tid / TPQ;
   const int d0 = (tid - qi * TPQ) * kF32Dims;   // this lane's first head dim
@@ -845,7 +1341,19 @@ hipError_t launch_prefill_attention(const AttnPlan& p, hipStream_t s) {
   if (p.bf16) {
     a.n_qtiles = (p.T + kBM - 1) / kBM;
     const int blocks = set_classes(p, a);
-    if (p.sel) {
+    if (!p.sel && p.W == 0) {
+      // persistent blocks, one per compute unit, a multiple of 8 (one per XCD
+      // slot), at most one per 8 items
+      int dev = 0, cus = 0;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return hipErrorInvalidDevice;
+      const int per_xcd = std::max(1, std::min(cus / 8, (blocks + 7) / 8));
+      if (p.Dh == 128)
+        hipLaunchKernelGGL((attn_bf16_stream_kernel<128>), dim3(8 * per_xcd), dim3(kWaves * 64), 0, s, a);
+      else
+        hipLaunchKernelGGL((attn_bf16_stream_kernel<64>), dim3(8 * per_xcd), dim3(kWaves * 64), 0, s, a);
+    } else if (p.sel) {
       if (p.Dh == 128)
         hipLaunchKernelGGL((attn_bf16_kernel<128, true>), dim3(blocks), dim3(kWaves * 64), 0, s, a);
       else
