@@ -598,13 +598,18 @@ def measure_copy(torch):
 # offline: rocprofv3 CSV output -> short summaries under profiles/ (CPU only)
 # ---------------------------------------------------------------------------
 
-KERNEL_PATTERNS = {"scan": ("scan_kernel", "scan_seg_kernel"), "attention": "attn_bf16_kernel",
+KERNEL_PATTERNS = {"scan": ("scan_kernel", "scan_seg_kernel"), "attention": ("attn_bf16_kernel", "attn_bf16_stream_kernel"),
                    "attention_f32": "attn_f32_kernel",
                    "decode": "decode_kernel",
                    "topk_attend": "topk_attend_kernel", "topk_stats": "topk_stats_kernel",
                    "topk_append": "topk_append_kernel", "grid_to_col": "grid_to_col_kernel",
                    "ring_prefix": "ring_prefix_kernel", "topk_select": "topk_select_tile_kernel"}
 COPY_BYTES = 1 << 30   # --calibrate-copy: bytes read and bytes written by one copy
+
+
+def _pat_text(pat):
+    """The kernel-name pattern(s) as text."""
+    return pat if isinstance(pat, str) else " or ".join(pat)
 
 
 def _matches(name, pat):
@@ -660,7 +665,7 @@ def summarize_pmc(kernel, workload, fetch_dir, write_dir, cfetch_dir, cwrite_dir
         json.dump(out, fh, indent=1)
         fh.write("\n")
     with open(base + ".txt", "w") as fh:
-        fh.write(f"HBM traffic of {kernel} ({pat}) on workload {workload}\n\n")
+        fh.write(f"HBM traffic of {kernel} ({_pat_text(pat)}) on workload {workload}\n\n")
         fh.write("\n".join("$ " + c for c in cmds) + "\n\n")
         fh.write(f"dispatches averaged: FETCH {len(fetch)}, WRITE {len(write)}\n")
         fh.write(f"FETCH_SIZE {fk:.1f} KiB/dispatch x {f_fetch:.3f} (1 GiB copy read {cf:.1f} KiB)\n")
@@ -691,7 +696,7 @@ def summarize_counters(kernel, workload, dirs, bench_args):
                     f"python3 bench.py {bench_args}")
     cmds.append(f"python3 bench.py --summarize-counters {kernel} {workload} {' '.join(dirs)} "
                 f"--pmc-bench-args '{bench_args}'")
-    lines = [f"SQ counters of {kernel} ({pat}) on workload {workload}, per dispatch", ""]
+    lines = [f"SQ counters of {kernel} ({_pat_text(pat)}) on workload {workload}, per dispatch", ""]
     lines += ["$ " + c for c in cmds] + [""]
     lines += [f"{c:28s} {v:.4g}" for c, v in sorted(vals.items())]
     g = vals.get
@@ -723,7 +728,7 @@ def summarize_trace(trace_dir, kernel, workload, bench_args):
     pat = KERNEL_PATTERNS[kernel]
     with open(path) as fh:
         rows = [r for r in csv.DictReader(fh) if _matches(r["Name"], pat)]
-    lines = [f"rocprofv3 kernel statistics of {kernel} ({pat}) on workload {workload}", "",
+    lines = [f"rocprofv3 kernel statistics of {kernel} ({_pat_text(pat)}) on workload {workload}", "",
              f"$ rocprofv3 --kernel-trace --stats --output-format csv -d {trace_dir} -o kt -- python3 bench.py "
              f"{bench_args}",
              f"$ python3 bench.py --summarize-trace {trace_dir} {kernel} {workload} --pmc-bench-args '{bench_args}'",
