@@ -672,9 +672,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_bf16_kernel(const AttnArg
 // 32 query rows: the next q-tile's Q rows land there by direct loads while
 // the current q-tile runs and are read into fragments once its last tile's
 // scores are taken (the old fragments are dead then); the current q-tile's
-// output rows are staged there after that and stored as whole rows.  The Q
-// rows of the q-tile after the next wait until the area is free again, so
-// the loads run at most one q-tile ahead.
+// output rows are staged there after that and stored as whole rows at the
+// start of the next step, under that step's work.  The Q rows of the q-tile
+// after the next wait until the area is free again, so the loads run at most
+// one q-tile ahead.  q-tiles whose rows have no key get their zero rows when
+// the list reaches them.
 //
 // Item order: within an XCD (blocks and items are dealt to the XCDs by index
 // mod 8, which keeps every (b, h) pair on one XCD as in the plain launch) the
