@@ -60,3 +60,35 @@ def test_grid_only_qtile_stream_planted_keys():
     """Index-sensitive check at a many-q-tile grid-only shape with mixed
     dilations (1024 q-tiles: four per block)."""
     assert _planted_check(16384, 16, 128, [16] * 8 + [64] * 4 + [4] * 4, 0, 100, 23, head_group=16) <= BF16_TOL
+
+
+def test_grid_only_chunk_at_offset():
+    """rat_prefill_chunk without a window: a 4096-row chunk, then an
+    8192-row chunk at position 4096 (16 heads: 512 q-tiles, two per block,
+    key positions offset from the query rows) against the oracle's prefill
+    of the whole sequence on sampled rows of the second chunk."""
+    R = need_gpu()
+    B, H, Dh = 1, 16, 128
+    dil = [16] * 8 + [64] * 4 + [4] * 4
+    chunks = [4096, 8192]
+    L = sum(chunks)
+    x = inputs.prefill_inputs(B, L, H, Dh, dtype=torch.bfloat16, seed=77)
+    max_pos = L + 64
+    off, cap, nrows = R.rat_grid_layout(H, dil, max_pos)
+    grid_k = torch.zeros(B * nrows * Dh, dtype=torch.bfloat16, device=DEV)
+    grid_v = torch.zeros(B * nrows * Dh, dtype=torch.bfloat16, device=DEV)
+    state_k = torch.zeros((B, H, Dh), dtype=torch.float32, device=DEV)
+    state_v = torch.zeros((B, H, Dh), dtype=torch.float32, device=DEV)
+    p0 = 0
+    outs = []
+    for T in chunks:
+        d = {n: t[:, p0:p0 + T].contiguous().to(DEV) for n, t in x.items()}
+        outs.append(R.rat_prefill_chunk(d["q"], d["k"], d["v"], d["zk"], d["zv"], state_k, state_v, grid_k, grid_v,
+                                        off, cap, None, None, p0, max_pos, dil, 0))
+        p0 += T
+    torch.cuda.synchronize()
+    rows = _wave_rows(chunks[1], seed=5)
+    ref = oracle.prefill(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["zk"]), f64(x["zv"]), dil, 0,
+                         rows=[chunks[0] + r for r in rows])
+    err = report("chunk p0=4096", f64(outs[1])[:, rows], ref[:, [chunks[0] + r for r in rows]], rms_max=RMS_TOL)
+    assert err <= BF16_TOL
