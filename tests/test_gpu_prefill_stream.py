@@ -56,10 +56,11 @@ def test_grid_only_qtile_stream(B, H, Dh, T, dil):
                 assert torch.count_nonzero(out[:, t, h]).item() == 0, (t, h)
 
 
-def test_grid_only_qtile_stream_planted_keys():
+@pytest.mark.parametrize("Dh,seed", [(128, 23), (64, 24)])
+def test_grid_only_qtile_stream_planted_keys(Dh, seed):
     """Index-sensitive check at a many-q-tile grid-only shape with mixed
-    dilations (1024 q-tiles: four per block)."""
-    assert _planted_check(16384, 16, 128, [16] * 8 + [64] * 4 + [4] * 4, 0, 100, 23, head_group=16) <= BF16_TOL
+    dilations (1024 q-tiles: four per block), both head sizes."""
+    assert _planted_check(16384, 16, Dh, [16] * 8 + [64] * 4 + [4] * 4, 0, 100, seed, head_group=16) <= BF16_TOL
 
 
 def test_grid_only_chunk_at_offset():
